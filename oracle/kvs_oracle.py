@@ -1,0 +1,323 @@
+"""fp64 reference for every step of the decode path (test infrastructure only).
+
+All floating-point inputs are converted exactly to float64 by the caller
+(fp16 and bf16 values are exactly representable).  Integer work is done with
+Python integers or exact rationals.  Functions are written per head / per
+group so that each can be checked by eye against its definition; none is
+blocked, fused or reordered beyond what its definition states.
+
+Notation (shared with the pages): P tokens per page, Hp KV heads per ragged
+page group, G = Hkv / Hp groups per layer, Gq = Hq / Hkv query heads per KV
+head, n retained tokens of a head, np = ceil(n / P) logical pages of a head.
+"""
+
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+from typing import List, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "retained_count",
+    "cluster_heads",
+    "group_members",
+    "group_page_count",
+    "page_minmax",
+    "page_scores",
+    "topk_pages",
+    "split_weight",
+    "plan_split_layer",
+    "plan_split",
+    "split_bounds",
+    "split_of_unit",
+    "page_token_ids",
+    "attention",
+    "attention_lse",
+    "lse_combine",
+    "group_units",
+    "decode_group_split",
+    "decode_head",
+]
+
+
+# ---------------------------------------------------------------------------
+# Retention and grouping -- Tangram review, 3.1 Budget Reservation and
+# 3.2 Ragged Paging.
+# ---------------------------------------------------------------------------
+
+def retained_count(budget: float, context: int) -> int:
+    """Tokens a head keeps: the ceiling of B * N (Tangram review, 3.1, the
+    Top(ceil(B N), s) selection rule), with B in (0, 1].
+
+    Evaluated on the exact binary value of ``budget`` with rationals, so no
+    floating-point rounding can move the ceiling.
+    """
+    b = Fraction(budget)
+    if not (0 < b <= 1):
+        raise ValueError("budget must lie in (0, 1]")
+    if context < 1:
+        raise ValueError("context must be >= 1")
+    return math.ceil(b * context)
+
+
+def cluster_heads(budgets: Sequence[float], Hp: int) -> np.ndarray:
+    """Budget-aware clustering (Tangram review, 3.2): heads of similar
+    retention share a page group.
+
+    Reading used (the pages give no formula): order the KV heads of one layer
+    by budget, largest first, equal budgets by lower head index; the head at
+    sorted position ``pos`` goes to group ``pos // Hp``, slot ``pos % Hp``.
+    Returns ``head_slot[h] = pos``.
+    """
+    Hkv = len(budgets)
+    if Hkv % Hp:
+        raise ValueError("Hkv must be a multiple of Hp")
+    order = sorted(range(Hkv), key=lambda h: (-float(budgets[h]), h))
+    head_slot = np.empty(Hkv, dtype=np.int64)
+    for pos, h in enumerate(order):
+        head_slot[h] = pos
+    return head_slot
+
+
+def group_members(head_slot: Sequence[int], Hp: int) -> List[List[int]]:
+    """Heads of each group in slot order: group i holds slots [i*Hp, (i+1)*Hp)."""
+    Hkv = len(head_slot)
+    by_slot = [None] * Hkv
+    for h, s in enumerate(head_slot):
+        by_slot[int(s)] = h
+    if any(x is None for x in by_slot):
+        raise ValueError("head_slot must be a permutation")
+    return [by_slot[i * Hp:(i + 1) * Hp] for i in range(Hkv // Hp)]
+
+
+def group_page_count(n_of_heads: Sequence[int], P: int) -> int:
+    """Pages a group is allocated: enough for its longest head (Tangram
+    review, 3.2: each group is sized by the largest budget inside it)."""
+    return -(-max(int(n) for n in n_of_heads) // P)
+
+
+# ---------------------------------------------------------------------------
+# Page metadata and scoring -- FlexiCache summary, Core method (Quest-style
+# min-max key bound) and Key observations, assumption 2 (MinMax cache).
+# ---------------------------------------------------------------------------
+
+def page_token_ids(p: int, n: int, P: int) -> range:
+    """Valid token positions of logical page p of a head holding n tokens."""
+    return range(p * P, min(n, (p + 1) * P))
+
+
+def page_minmax(K: np.ndarray, P: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-page, per-channel minimum and maximum of the keys.
+
+    ``K`` is the head's retained keys [n][d] in float64.  Page p covers
+    tokens [p*P, min(n, (p+1)*P)); a partial last page uses its valid tokens
+    only.  Returns (kmin, kmax), each [np][d].
+    """
+    K = np.asarray(K, dtype=np.float64)
+    n, d = K.shape
+    npg = -(-n // P)
+    kmin = np.empty((npg, d))
+    kmax = np.empty((npg, d))
+    for p in range(npg):
+        rows = K[p * P:min(n, (p + 1) * P)]
+        kmin[p] = rows.min(axis=0)
+        kmax[p] = rows.max(axis=0)
+    return kmin, kmax
+
+
+def page_scores(q_group: np.ndarray, kmin: np.ndarray, kmax: np.ndarray) -> np.ndarray:
+    """Quest-style page score of one KV head (FlexiCache summary, Core method).
+
+    For query row g and page p the bound is sum_d max(q[g,d]*kmin[p,d],
+    q[g,d]*kmax[p,d]), an upper bound on q[g]·k for every key k of the page.
+    The head's score is the largest bound over the query heads of its GQA
+    group (reading: the per-KV-head score is max-reduced over the group).
+    No 1/sqrt(d) scale: a positive scale does not change the ranking.
+    Returns s[np] in float64.
+    """
+    q = np.asarray(q_group, dtype=np.float64)
+    lo = np.asarray(kmin, dtype=np.float64)
+    hi = np.asarray(kmax, dtype=np.float64)
+    # bound[g, p] for every query row g and page p; then the max over g.
+    bound = np.stack([np.maximum(q[g] * lo, q[g] * hi).sum(axis=1)
+                      for g in range(q.shape[0])])
+    return bound.max(axis=0)
+
+
+def topk_pages(scores: Sequence[float], K: int) -> np.ndarray:
+    """Per-KV-head top-K page selection (FlexiCache summary, Core method).
+
+    Keeps the min(K, np) pages with the largest score; equal scores go to the
+    lower page index.  The kept pages are returned in ascending page order.
+    The comparison is done in whatever precision ``scores`` carries (pass
+    float32-rounded scores to decide in the kernel's precision).
+    """
+    if K < 1:
+        raise ValueError("K must be >= 1")
+    s = [float(x) for x in scores]
+    ranked = sorted(range(len(s)), key=lambda p: (-s[p], p))
+    return np.array(sorted(ranked[:min(K, len(s))]), dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
+# Ahead-of-time split plan -- Tangram review, 3.3 AOT Load Balancing.
+# ---------------------------------------------------------------------------
+
+def split_weight(budget: float, cap: float = 0.0) -> int:
+    """Integer weight of a head: round(min(B, cap) * 2^20), halves rounded up.
+
+    ``cap <= 0`` means no cap.  The 2^-20 grid lets the planner compare
+    group loads exactly in integers.  Evaluated with exact rationals.
+    """
+    b = Fraction(budget)
+    if cap > 0:
+        b = min(b, Fraction(cap))
+    return math.floor(b * (1 << 20) + Fraction(1, 2))
+
+
+def plan_split_layer(phi: Sequence[int], T: int) -> List[int]:
+    """Split counts of one layer's groups (Tangram review, 3.3).
+
+    The pages state only the goal: workgroups are handed out in proportion to
+    each group's aggregated budget, so bigger groups get more and the load per
+    workgroup is even.  Reading used: highest-averages (D'Hondt)
+    apportionment -- every group starts with one split; each further split
+    goes to the group with the largest load per split phi_i / S_i, compared
+    exactly as phi_i * S_j vs phi_j * S_i, equal loads to the lower index.
+    """
+    G = len(phi)
+    if T < G:
+        raise ValueError("T must be >= number of groups")
+    S = [1] * G
+    for _ in range(T - G):
+        best = 0
+        for i in range(1, G):
+            if phi[i] * S[best] > phi[best] * S[i]:
+                best = i
+        S[best] += 1
+    return S
+
+
+def plan_split(budgets: np.ndarray, head_slot: np.ndarray, Hp: int,
+               cap: float, T: int) -> np.ndarray:
+    """Static split map S[L][G] (Tangram review, 3.3: one row per layer, one
+    column per head group).  Group load phi_i = sum of its heads' weights."""
+    budgets = np.asarray(budgets)
+    L, Hkv = budgets.shape
+    G = Hkv // Hp
+    S = np.zeros((L, G), dtype=np.int64)
+    for l in range(L):
+        phi = [0] * G
+        for h in range(Hkv):
+            phi[int(head_slot[l][h]) // Hp] += split_weight(budgets[l][h], cap)
+        S[l] = plan_split_layer(phi, T)
+    return S
+
+
+# ---------------------------------------------------------------------------
+# Attention, split and combine -- FlexiCache summary, Core method (sparse
+# flash-decoding over the selected pages).
+# ---------------------------------------------------------------------------
+
+def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """Plain softmax attention of one query row over m tokens:
+    softmax(scale * K q) V, in float64."""
+    o, _ = attention_lse(q, K, V, scale)
+    return o
+
+
+def attention_lse(q: np.ndarray, K: np.ndarray, V: np.ndarray,
+                  scale: float) -> Tuple[np.ndarray, float]:
+    """Attention of one query row plus the log of its softmax denominator.
+
+    z_t = scale * q·k_t, m = max z, l = sum exp(z - m), o = sum exp(z - m) v / l,
+    lse = m + ln l.  With no tokens the result is (0, -inf).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    if K.shape[0] == 0:
+        return np.zeros(V.shape[1] if V.ndim == 2 else q.shape[0]), -math.inf
+    z = scale * (K @ q)
+    m = float(z.max())
+    w = np.exp(z - m)
+    ell = float(w.sum())
+    return (w @ V) / ell, m + math.log(ell)
+
+
+def lse_combine(parts: Sequence[Tuple[np.ndarray, float]]) -> Tuple[np.ndarray, float]:
+    """Merge partial results of disjoint token sets: with M = max lse_s,
+    o = sum exp(lse_s - M) o_s / sum exp(lse_s - M), lse = M + ln(sum ...).
+    Parts with lse = -inf (no tokens) carry no weight."""
+    live = [(o, lse) for o, lse in parts if lse != -math.inf]
+    if not live:
+        raise ValueError("no non-empty part")
+    M = max(lse for _, lse in live)
+    num = sum(math.exp(lse - M) * np.asarray(o, dtype=np.float64) for o, lse in live)
+    den = sum(math.exp(lse - M) for _, lse in live)
+    return num / den, M + math.log(den)
+
+
+def split_bounds(U: int, S: int) -> List[Tuple[int, int]]:
+    """Unit ranges of S splits over U units: split s covers
+    [floor(s U / S), floor((s+1) U / S))."""
+    return [((s * U) // S, ((s + 1) * U) // S) for s in range(S)]
+
+
+def split_of_unit(u: int, U: int, S: int) -> int:
+    """The split whose range (as in ``split_bounds``) contains unit u,
+    found by scanning the ranges."""
+    for s, (a, b) in enumerate(split_bounds(U, S)):
+        if a <= u < b:
+            return s
+    raise ValueError("unit out of range")
+
+
+def group_units(attended: Sequence[Sequence[int]]) -> List[Tuple[int, int]]:
+    """Work units of one (request, group): head-major over the group's slots,
+    then the slot's attended pages in list order -> [(slot, page), ...]."""
+    return [(j, int(p)) for j, pages in enumerate(attended) for p in pages]
+
+
+def decode_group_split(q_slots: Sequence[np.ndarray], K_slots: Sequence[np.ndarray],
+                       V_slots: Sequence[np.ndarray], attended: Sequence[Sequence[int]],
+                       P: int, S: int, scale: float) -> List[np.ndarray]:
+    """Split-K decode of one (request, group) with S splits, then LSE combine.
+
+    q_slots[j] is [Gq][d] (the query heads of the head in slot j), K_slots[j]
+    and V_slots[j] are that head's retained tokens [n_j][d], attended[j] its
+    attended logical pages.  Split s processes its contiguous range of the
+    head-major unit list; for every head it touches it produces a partial
+    (o, lse) over that head's valid tokens in the range; the partials of each
+    query head are then merged with ``lse_combine``.  Returns [Gq][d] per slot.
+    """
+    units = group_units(attended)
+    U = len(units)
+    out = []
+    for j in range(len(q_slots)):
+        n_j = K_slots[j].shape[0]
+        rows = []
+        for g in range(q_slots[j].shape[0]):
+            parts = []
+            for a, b in split_bounds(U, S):
+                toks = [t for (jj, p) in units[a:b] if jj == j
+                        for t in page_token_ids(p, n_j, P)]
+                if toks:
+                    parts.append(attention_lse(q_slots[j][g], K_slots[j][toks],
+                                               V_slots[j][toks], scale))
+            rows.append(lse_combine(parts)[0])
+        out.append(np.stack(rows))
+    return out
+
+
+def decode_head(q_group: np.ndarray, K: np.ndarray, V: np.ndarray,
+                pages: Sequence[int], P: int, scale: float) -> np.ndarray:
+    """Attention of a KV head's query group over the valid tokens of its
+    attended pages (the result split-K + combine reaches up to rounding).
+    Returns [Gq][d]."""
+    n = K.shape[0]
+    toks = [t for p in pages for t in page_token_ids(int(p), n, P)]
+    return np.stack([attention(q_group[g], K[toks], V[toks], scale)
+                     for g in range(q_group.shape[0])])
