@@ -1,0 +1,198 @@
+/*
+ * kvs.h -- C ABI of libkvs.so: decode attention over a head-ragged paged KV
+ * cache with min-max page scoring and per-KV-head top-K page selection,
+ * written for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (cited by page title and section):
+ *   [T] "Tangram: Unlocking Non-Uniform KV Cache Compression for Efficient
+ *       Multi-turn LLM Serving" (paper review): 3.1 Budget Reservation,
+ *       3.2 Ragged Paging, 3.3 AOT Load Balancing.
+ *   [F] "FlexiCache: Leveraging Temporal Stability of Attention Heads for
+ *       Efficient KV Cache Management (MLSys 2026)" (paper summary): Core
+ *       method (sparse decode, Quest-style min-max page bound), System
+ *       engineering (per-head-layer block table with null blocks), Key
+ *       observations, assumption 2 (GPU-resident MinMax cache).
+ *
+ * Conventions shared by every call
+ *   - Return value: KVS_OK (0) or a negative KVS_E* code.  On error no kernel
+ *     was launched and kvs_last_error() (thread-local) holds a message.  A
+ *     failed launch returns KVS_EHIP with the HIP error text.
+ *   - Device calls are asynchronous and ordered on `stream` (a hipStream_t
+ *     passed as void*; NULL = the default stream).  Host-only calls are
+ *     synchronous and touch no device.
+ *   - Ownership: the caller owns every buffer.  The library allocates no
+ *     device memory and keeps no pointer after a call returns; scratch space
+ *     comes from the caller's `workspace`.  Calls are reentrant.
+ *   - Layout is row-major C order throughout.  Element types: KV, min-max
+ *     and queries are fp16 or bf16 (`dtype`), scores and outputs fp32,
+ *     indices int32.  Device pointers must be 16-byte aligned.
+ *   - Contents of device-resident integer inputs (seq_len, page_table, sel)
+ *     cannot be checked before launch.  Kernels never read outside the
+ *     buffers described here: a page id outside [0, num_pages) or a
+ *     negative id is treated as a null page and skipped; seq_len is clamped
+ *     to [0, P*max_group_pages]; sel_count is clamped to [0, K].
+ */
+#ifndef KVS_H_
+#define KVS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  KVS_OK = 0,
+  KVS_EINVAL = -1,        /* bad argument (null, misaligned, out of range) */
+  KVS_EUNSUPPORTED = -2,  /* valid but not built: head_dim, page size, dtype, GQA */
+  KVS_EHIP = -3,          /* HIP runtime error */
+  KVS_ENOSPC = -4         /* caller's workspace too small */
+};
+
+enum { KVS_F16 = 0, KVS_BF16 = 1 };
+
+/*
+ * One layer's head-ragged paged KV cache [T 3.2; F System engineering].
+ *
+ * KV heads are cut into G = Hkv/Hp groups of Hp heads; each group has its
+ * own page table.  A physical page holds, for each of the group's Hp heads,
+ * P tokens of K followed by P tokens of V:
+ *     kv[num_pages][Hp][2][P][d]         (index 2: 0 = K, 1 = V)
+ * so one head's K tile of a page is P*d contiguous elements.
+ * A group is allocated pages for its longest head [T 3.2]; shorter heads of
+ * the group leave the tail of their slots unused.
+ *
+ *   kv          device, [num_pages][Hp][2][P][d] dtype.
+ *   minmax      device, [num_pages][Hp][2][d] dtype: per page and slot, the
+ *               per-channel minimum (row 0) and maximum (row 1) of the valid
+ *               keys [F Key observations, assumption 2].  Written by
+ *               kvs_build_minmax, read by kvs_score_pages.
+ *   page_table  device, [b][G][max_group_pages] int32 physical page ids;
+ *               -1 marks a null entry [F System engineering].  Logical page
+ *               p of head h covers its tokens [p*P, (p+1)*P).
+ *   seq_len     device, [b][Hkv] int32: n, the tokens head h of request r
+ *               retained (ceil(B*N) under Budget Reservation [T 3.1]),
+ *               1 <= n <= P*max_group_pages.
+ *   head_slot   device, [Hkv] int32: head h sits in group head_slot[h]/Hp,
+ *               slot head_slot[h]%Hp; a permutation of [0, Hkv).
+ *   b, Hq, Hkv  requests, query heads, KV heads (Hq % Hkv == 0).
+ *   Hp          heads per page group (Hkv % Hp == 0, G <= 64).
+ *   d           head dimension: 128 or 256.
+ *   P           tokens per page: 16.
+ *   dtype       KVS_F16 or KVS_BF16.
+ */
+typedef struct kvs_paged_kv {
+  const void* kv;
+  void* minmax;
+  const int32_t* page_table;
+  const int32_t* seq_len;
+  const int32_t* head_slot;
+  int32_t b, Hq, Hkv, Hp, d, P, max_group_pages, num_pages, dtype;
+} kvs_paged_kv;
+
+/*
+ * Build the min-max page metadata [F Key observations, assumption 2; Core
+ * method].  For every request r, head h and logical page p < ceil(n/P):
+ * minmax[page][slot][0][c] = min and [1][c] = max over the page's valid
+ * tokens t in [p*P, min(n, (p+1)*P)) of K[t][c].  Exact (a selection).
+ * Entries of slots or pages beyond a head's n are left untouched.
+ * Runs once per page fill, not per decode step.
+ */
+int kvs_build_minmax(const kvs_paged_kv* cache, void* stream);
+
+/*
+ * Quest-style page scores [F Core method].  For request r, KV head h and
+ * logical page p < ceil(n/P):
+ *   scores[r][h][p] = max over the Gq query heads g of h of
+ *                     sum_c max(q[r][g][c]*kmin[c], q[r][g][c]*kmax[c])
+ * (no 1/sqrt(d) scale), fp32 products of the fp16/bf16 inputs (exact) summed
+ * in a fixed order.  Pages p >= ceil(n/P) get -inf.
+ *   q       device, [b][Hq][d] dtype; query head g belongs to KV head g/Gq.
+ *   scores  device, [b][Hkv][max_group_pages] fp32, fully written.
+ */
+int kvs_score_pages(const kvs_paged_kv* cache, const void* q, float* scores, void* stream);
+
+/*
+ * Per-KV-head top-K page selection [F Core method].  For each (r, h) with
+ * np = ceil(seq_len[r][h]/P) pages: keep the min(K, np) pages of largest
+ * score, equal scores going to the lower page index, and write them in
+ * ascending page order.  Integer keys built from the fp32 bits (value
+ * order; -0 and +0 are equal).  Deterministic.
+ *   scores     device, [b][Hkv][max_pages] fp32 (entries >= np ignored).
+ *   seq_len    device, [b][Hkv] int32.
+ *   K          1 <= K <= 1024.  max_pages <= 8192.
+ *   sel        device, [b][Hkv][K] int32; entries >= sel_count are -1.
+ *   sel_count  device, [b][Hkv] int32 = min(K, np).
+ */
+int kvs_topk_pages(const float* scores, const int32_t* seq_len, int32_t P, int32_t b,
+                   int32_t Hkv, int32_t max_pages, int32_t K, int32_t* sel,
+                   int32_t* sel_count, void* stream);
+
+/*
+ * Ahead-of-time workload split map [T 3.3], host only.
+ * Per layer l: weight w_h = round(min(B[l][h], cap) * 2^20) (cap <= 0: no
+ * cap), group load phi_i = sum of w_h over the heads with head_slot/Hp == i,
+ * then T splits are apportioned by highest averages (D'Hondt): every group
+ * starts with 1, each further split goes to the largest phi_i/S_i (exact
+ * integer comparison, equal loads to the lower i).  This minimises the
+ * largest load per split; the page states only that goal and the
+ * proportionality, not the algorithm.
+ *   budgets    host, [L][Hkv] in (0, 1].
+ *   head_slot  host, [L][Hkv], each row a permutation of [0, Hkv).
+ *   T          splits per request per layer, G <= T <= 65536.
+ *   S          host out, [L][G] int32, each row sums to T.
+ */
+int kvs_plan_split(const double* budgets, const int32_t* head_slot, int32_t L, int32_t Hkv,
+                   int32_t Hp, double cap, int32_t T, int32_t* S);
+
+/*
+ * Ragged split-K decode attention plus LSE combine [F Core method; T 3.2,
+ * 3.3].  For request r and group i the work units are the group's (slot,
+ * page) pairs, head-major: slot 0's attended pages in list order, then slot
+ * 1's, ...  A head attends its sel list (sel_count entries) when sel is
+ * non-NULL, else all of its ceil(n/P) pages.  With U units and S_i =
+ * S_row[i] splits, split s takes units [floor(s*U/S_i), floor((s+1)*U/S_i)).
+ * One workgroup per (r, i, s) computes, for every query head of every head
+ * it touches, softmax(scale * q.k) v over the valid tokens of its units and
+ * the log-sum-exp; a second kernel merges the splits of each query head:
+ *   out[r][g] = sum_s e^{lse_s - M} o_s / sum_s e^{lse_s - M}, M = max lse_s.
+ *   q          device, [b][Hq][d] dtype.
+ *   sel        device, [b][Hkv][K] int32 or NULL; sel_count device [b][Hkv].
+ *   K          row length of sel (ignored when sel is NULL).
+ *   S_row      host, [G] int32, each >= 1, sum <= 65536; b*sum(S_row)
+ *              workgroups are launched.
+ *   scale      softmax scale, usually 1/sqrt(d).
+ *   workspace  device scratch of at least kvs_decode_workspace_bytes(...)
+ *              bytes, 256-byte aligned; contents on entry do not matter.
+ *   out        device, [b][Hq][d] fp32.
+ */
+int kvs_decode_attn(const kvs_paged_kv* cache, const void* q, const int32_t* sel,
+                    const int32_t* sel_count, int32_t K, const int32_t* S_row, float scale,
+                    void* workspace, size_t ws_bytes, float* out, void* stream);
+
+/* Bytes of workspace kvs_decode_attn needs for this shape and split row
+ * (per-split partial outputs and log-sum-exps).  0 on bad arguments. */
+size_t kvs_decode_workspace_bytes(int32_t b, int32_t Hq, int32_t d, const int32_t* S_row,
+                                  int32_t G);
+
+/* Concurrent decode workgroups on `device` for this kernel variant [T 3.3:
+ * the split map is sized to what the chip runs at once]:
+ * *W = compute units x max resident workgroups per compute unit. */
+int kvs_decode_concurrency(int32_t device, int32_t d, int32_t gqa, int32_t dtype, int32_t* W);
+
+/* Budget-aware clustering [T 3.2], host only: per layer, heads ordered by
+ * budget (largest first, equal budgets by lower head index); the head at
+ * sorted position pos gets head_slot = pos (group pos/Hp, slot pos%Hp).
+ *   budgets [L][Hkv] host; head_slot [L][Hkv] host out. */
+int kvs_cluster_heads(const double* budgets, int32_t L, int32_t Hkv, int32_t Hp,
+                      int32_t* head_slot);
+
+/* Message of the last error on this thread ("" if none). */
+const char* kvs_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVS_H_ */

@@ -1,0 +1,215 @@
+// C-ABI entry points of libkvs: argument validation (before any HIP call),
+// error reporting, workspace sizing and the kernel launches.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "kvs_internal.h"
+
+namespace kvs {
+
+namespace {
+thread_local char g_err[512] = "";
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int hip_error(hipError_t e, const char* what) {
+  return set_error(KVS_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Validates the cache descriptor.  need_minmax: the call reads or writes it.
+int check_cache(const kvs_paged_kv* p, bool need_minmax, const char* fn, CacheView* v) {
+  if (!p) return set_error(KVS_EINVAL, "%s: cache descriptor is NULL", fn);
+  if (!p->kv || !p->page_table || !p->seq_len || !p->head_slot || (need_minmax && !p->minmax))
+    return set_error(KVS_EINVAL, "%s: null device pointer in cache descriptor", fn);
+  if (!aligned16(p->kv) || (need_minmax && !aligned16(p->minmax)))
+    return set_error(KVS_EINVAL, "%s: kv and minmax must be 16-byte aligned", fn);
+  if (p->b < 1 || p->Hkv < 1 || p->Hq < 1 || p->Hp < 1 || p->max_group_pages < 1 ||
+      p->num_pages < 1)
+    return set_error(KVS_EINVAL, "%s: sizes must be positive", fn);
+  if (p->Hq % p->Hkv) return set_error(KVS_EINVAL, "%s: Hq %% Hkv != 0", fn);
+  if (p->Hkv % p->Hp) return set_error(KVS_EINVAL, "%s: Hkv %% Hp != 0", fn);
+  if (p->Hkv > kMaxHkv || p->Hp > kMaxHp || p->Hkv / p->Hp > kMaxGroups)
+    return set_error(KVS_EUNSUPPORTED, "%s: need Hkv <= %d, Hp <= %d, G <= %d", fn, kMaxHkv,
+                     kMaxHp, kMaxGroups);
+  const int gq = p->Hq / p->Hkv;
+  if (gq != 1 && gq != 2 && gq != 4 && gq != 8)
+    return set_error(KVS_EUNSUPPORTED, "%s: query group size %d not in {1,2,4,8}", fn, gq);
+  if (p->d != 128 && p->d != 256)
+    return set_error(KVS_EUNSUPPORTED, "%s: head_dim %d not in {128, 256}", fn, p->d);
+  if (p->P != 16) return set_error(KVS_EUNSUPPORTED, "%s: page size %d != 16", fn, p->P);
+  if (p->dtype != KVS_F16 && p->dtype != KVS_BF16)
+    return set_error(KVS_EUNSUPPORTED, "%s: dtype %d is neither f16 nor bf16", fn, p->dtype);
+  if ((int64_t)p->b * p->Hkv * p->max_group_pages > ((int64_t)1 << 40) ||
+      (int64_t)p->P * p->max_group_pages > 0x7fffffff)
+    return set_error(KVS_EINVAL, "%s: cache too large", fn);
+  v->kv = p->kv;
+  v->minmax = p->minmax;
+  v->page_table = p->page_table;
+  v->seq_len = p->seq_len;
+  v->head_slot = p->head_slot;
+  v->b = p->b;
+  v->Hq = p->Hq;
+  v->Hkv = p->Hkv;
+  v->Hp = p->Hp;
+  v->G = p->Hkv / p->Hp;
+  v->Gq = gq;
+  v->d = p->d;
+  v->P = p->P;
+  v->maxpg = p->max_group_pages;
+  v->num_pages = p->num_pages;
+  v->dtype = p->dtype;
+  return KVS_OK;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Partial outputs then log-sum-exps: [b][Hq][Smax][d] f32, [b][Hq][Smax] f32.
+size_t workspace_bytes(int b, int Hq, int d, int Smax) {
+  const size_t rows = (size_t)b * Hq * Smax;
+  return round256(rows * d * sizeof(float)) + round256(rows * sizeof(float));
+}
+
+}  // namespace
+
+int set_error(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+}  // namespace kvs
+
+using namespace kvs;
+
+extern "C" const char* kvs_last_error(void) { return g_err; }
+
+extern "C" int kvs_build_minmax(const kvs_paged_kv* cache, void* stream) {
+  clear_error();
+  CacheView c;
+  if (int rc = check_cache(cache, true, "kvs_build_minmax", &c)) return rc;
+  if (hipError_t e = launch_minmax(c, (hipStream_t)stream)) return hip_error(e, "kvs_build_minmax");
+  return KVS_OK;
+}
+
+extern "C" int kvs_score_pages(const kvs_paged_kv* cache, const void* q, float* scores,
+                               void* stream) {
+  clear_error();
+  CacheView c;
+  if (int rc = check_cache(cache, true, "kvs_score_pages", &c)) return rc;
+  if (!q || !scores) return set_error(KVS_EINVAL, "kvs_score_pages: null q or scores");
+  if (!aligned16(q)) return set_error(KVS_EINVAL, "kvs_score_pages: q must be 16-byte aligned");
+  if (hipError_t e = launch_score(c, q, scores, (hipStream_t)stream))
+    return hip_error(e, "kvs_score_pages");
+  return KVS_OK;
+}
+
+extern "C" int kvs_topk_pages(const float* scores, const int32_t* seq_len, int32_t P, int32_t b,
+                              int32_t Hkv, int32_t max_pages, int32_t K, int32_t* sel,
+                              int32_t* sel_count, void* stream) {
+  clear_error();
+  if (!scores || !seq_len || !sel || !sel_count)
+    return set_error(KVS_EINVAL, "kvs_topk_pages: null pointer");
+  if (P != 16) return set_error(KVS_EUNSUPPORTED, "kvs_topk_pages: page size %d != 16", P);
+  if (b < 1 || Hkv < 1 || max_pages < 1)
+    return set_error(KVS_EINVAL, "kvs_topk_pages: sizes must be positive");
+  if (K < 1 || K > kMaxK)
+    return set_error(KVS_EINVAL, "kvs_topk_pages: K=%d not in [1, %d]", K, kMaxK);
+  if (max_pages > kMaxTopkPages)
+    return set_error(KVS_EUNSUPPORTED, "kvs_topk_pages: max_pages=%d > %d", max_pages,
+                     kMaxTopkPages);
+  if ((int64_t)b * Hkv > 0x7fffffff) return set_error(KVS_EINVAL, "kvs_topk_pages: b*Hkv too large");
+  if (hipError_t e = launch_topk(scores, seq_len, P, b, Hkv, max_pages, K, sel, sel_count,
+                                 (hipStream_t)stream))
+    return hip_error(e, "kvs_topk_pages");
+  return KVS_OK;
+}
+
+namespace {
+// Checks S_row and fills the split prefix sums; returns Smax via *smax.
+int check_splits(const int32_t* S_row, int G, int b, DecodeArgs* a, int* smax, const char* fn) {
+  if (!S_row) return set_error(KVS_EINVAL, "%s: S_row is NULL", fn);
+  int64_t acc = 0;
+  int mx = 0;
+  a->S_prefix[0] = 0;
+  for (int i = 0; i < G; ++i) {
+    if (S_row[i] < 1) return set_error(KVS_EINVAL, "%s: S_row[%d]=%d < 1", fn, i, S_row[i]);
+    acc += S_row[i];
+    if (acc > kMaxSplitsPerRequest)
+      return set_error(KVS_EINVAL, "%s: sum(S_row) > %d", fn, kMaxSplitsPerRequest);
+    a->S_prefix[i + 1] = (int)acc;
+    mx = S_row[i] > mx ? S_row[i] : mx;
+  }
+  if ((int64_t)b * acc > 0x7fffffff) return set_error(KVS_EINVAL, "%s: too many workgroups", fn);
+  a->splits_total = (int)acc;
+  *smax = mx;
+  return KVS_OK;
+}
+}  // namespace
+
+extern "C" size_t kvs_decode_workspace_bytes(int32_t b, int32_t Hq, int32_t d,
+                                             const int32_t* S_row, int32_t G) {
+  if (b < 1 || Hq < 1 || d < 1 || G < 1 || G > kMaxGroups || !S_row) return 0;
+  DecodeArgs a;
+  int smax = 0;
+  if (check_splits(S_row, G, b, &a, &smax, "kvs_decode_workspace_bytes")) return 0;
+  return workspace_bytes(b, Hq, d, smax);
+}
+
+extern "C" int kvs_decode_attn(const kvs_paged_kv* cache, const void* q, const int32_t* sel,
+                               const int32_t* sel_count, int32_t K, const int32_t* S_row,
+                               float scale, void* workspace, size_t ws_bytes, float* out,
+                               void* stream) {
+  clear_error();
+  const char* fn = "kvs_decode_attn";
+  DecodeArgs a;
+  memset(&a, 0, sizeof a);
+  if (int rc = check_cache(cache, false, fn, &a.c)) return rc;
+  if (!q || !out || !workspace) return set_error(KVS_EINVAL, "%s: null q, out or workspace", fn);
+  if (!aligned16(q) || !aligned16(out) || ((uintptr_t)workspace & 255u))
+    return set_error(KVS_EINVAL, "%s: q/out need 16-byte and workspace 256-byte alignment", fn);
+  if (sel && (!sel_count || K < 1 || K > kMaxK))
+    return set_error(KVS_EINVAL, "%s: with sel, need sel_count and 1 <= K <= %d", fn, kMaxK);
+  if (!(scale > 0.f) || !(scale < 1e30f)) return set_error(KVS_EINVAL, "%s: bad scale", fn);
+  int smax = 0;
+  if (int rc = check_splits(S_row, a.c.G, a.c.b, &a, &smax, fn)) return rc;
+  const size_t need = workspace_bytes(a.c.b, a.c.Hq, a.c.d, smax);
+  if (ws_bytes < need)
+    return set_error(KVS_ENOSPC, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+  a.q = q;
+  a.sel = sel;
+  a.sel_count = sel_count;
+  a.K = sel ? K : 0;
+  a.scale_log2 = scale * kLog2e;
+  a.Smax = smax;
+  a.o_part = static_cast<float*>(workspace);
+  a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                        round256((size_t)a.c.b * a.c.Hq * smax * a.c.d * 4));
+  a.out = out;
+  hipStream_t s = (hipStream_t)stream;
+  if (hipError_t e = launch_decode(a, s)) return hip_error(e, "kvs_decode_attn (split kernel)");
+  if (hipError_t e = launch_combine(a, s)) return hip_error(e, "kvs_decode_attn (combine kernel)");
+  return KVS_OK;
+}
+
+extern "C" int kvs_decode_concurrency(int32_t device, int32_t d, int32_t gqa, int32_t dtype,
+                                      int32_t* W) {
+  clear_error();
+  const char* fn = "kvs_decode_concurrency";
+  if (!W) return set_error(KVS_EINVAL, "%s: W is NULL", fn);
+  if (d != 128 && d != 256) return set_error(KVS_EUNSUPPORTED, "%s: head_dim %d", fn, d);
+  if (gqa != 1 && gqa != 2 && gqa != 4 && gqa != 8)
+    return set_error(KVS_EUNSUPPORTED, "%s: query group size %d", fn, gqa);
+  if (dtype != KVS_F16 && dtype != KVS_BF16)
+    return set_error(KVS_EUNSUPPORTED, "%s: dtype %d", fn, dtype);
+  int cus = 0, blocks = 0;
+  if (hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device))
+    return hip_error(e, fn);
+  if (hipError_t e = decode_blocks_per_cu(d, gqa, dtype, &blocks)) return hip_error(e, fn);
+  *W = cus * blocks;
+  return KVS_OK;
+}

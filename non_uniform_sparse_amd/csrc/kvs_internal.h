@@ -1,0 +1,59 @@
+// Internal declarations of libkvs: validated argument bundles passed to the
+// kernel launchers, error reporting and the launchers themselves.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/kvs.h"
+
+namespace kvs {
+
+constexpr int kMaxGroups = 64;     // G = Hkv / Hp
+constexpr int kMaxHp = 16;         // heads per page group
+constexpr int kMaxHkv = 128;
+constexpr int kMaxTopkPages = 8192;
+constexpr int kMaxK = 1024;
+constexpr int kMaxSplitsPerRequest = 65536;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Records a message for kvs_last_error() and returns `code`.
+int set_error(int code, const char* fmt, ...);
+void clear_error();
+
+// A validated kvs_paged_kv with derived sizes.
+struct CacheView {
+  const void* kv;
+  void* minmax;
+  const int32_t* page_table;
+  const int32_t* seq_len;
+  const int32_t* head_slot;
+  int b, Hq, Hkv, Hp, G, Gq, d, P, maxpg, num_pages, dtype;
+};
+
+struct DecodeArgs {
+  CacheView c;
+  const void* q;
+  const int32_t* sel;        // nullptr = every retained page
+  const int32_t* sel_count;
+  int K;
+  float scale_log2;          // softmax scale * log2(e): logits kept in base 2
+  float* o_part;             // [b][Hq][Smax][d]
+  float* lse_part;           // [b][Hq][Smax], base-2 log-sum-exp
+  int Smax;                  // max_i S_i
+  int splits_total;          // sum_i S_i
+  float* out;                // [b][Hq][d]
+  int S_prefix[kMaxGroups + 1];
+};
+
+hipError_t launch_minmax(const CacheView& c, hipStream_t s);
+hipError_t launch_score(const CacheView& c, const void* q, float* scores, hipStream_t s);
+hipError_t launch_topk(const float* scores, const int32_t* seq_len, int P, int b, int Hkv,
+                       int max_pages, int K, int32_t* sel, int32_t* sel_count, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_combine(const DecodeArgs& a, hipStream_t s);
+// Resident decode workgroups per compute unit for a kernel variant.
+hipError_t decode_blocks_per_cu(int d, int gqa, int dtype, int* blocks);
+
+}  // namespace kvs

@@ -1,0 +1,211 @@
+"""ctypes binding of libkvs.so.  Argument marshalling only: every step of
+the decode path runs in the library's HIP kernels or its C++ host code.
+Function names match the C entry points declared in include/kvs.h.
+
+Device buffers are torch tensors on a ROCm device; streams are torch
+streams (the current stream by default).  A missing library raises at
+first use -- there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvs.so")
+
+KVS_OK, KVS_EINVAL, KVS_EUNSUPPORTED, KVS_EHIP, KVS_ENOSPC = 0, -1, -2, -3, -4
+KVS_F16, KVS_BF16 = 0, 1
+
+# Every symbol include/kvs.h declares.
+EXPORTS = (
+    "kvs_build_minmax", "kvs_score_pages", "kvs_topk_pages", "kvs_plan_split",
+    "kvs_decode_attn", "kvs_decode_workspace_bytes", "kvs_decode_concurrency",
+    "kvs_cluster_heads", "kvs_last_error",
+)
+
+
+class KvsError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+class PagedKV(ctypes.Structure):
+    _fields_ = [
+        ("kv", ctypes.c_void_p),
+        ("minmax", ctypes.c_void_p),
+        ("page_table", ctypes.c_void_p),
+        ("seq_len", ctypes.c_void_p),
+        ("head_slot", ctypes.c_void_p),
+        ("b", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("Hp", ctypes.c_int32), ("d", ctypes.c_int32), ("P", ctypes.c_int32),
+        ("max_group_pages", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkvs.so (built in-tree by ``python -m non_uniform_sparse_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m non_uniform_sparse_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, f32, f64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_double
+        pkv = ctypes.POINTER(PagedKV)
+        L.kvs_build_minmax.argtypes = [pkv, vp]
+        L.kvs_score_pages.argtypes = [pkv, vp, vp, vp]
+        L.kvs_topk_pages.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
+        L.kvs_plan_split.argtypes = [vp, vp, i32, i32, i32, f64, i32, vp]
+        L.kvs_decode_attn.argtypes = [pkv, vp, vp, vp, i32, vp, f32, vp, ctypes.c_size_t, vp, vp]
+        L.kvs_decode_workspace_bytes.argtypes = [i32, i32, i32, vp, i32]
+        L.kvs_decode_workspace_bytes.restype = ctypes.c_size_t
+        L.kvs_decode_concurrency.argtypes = [i32, i32, i32, i32, vp]
+        L.kvs_cluster_heads.argtypes = [vp, i32, i32, i32, vp]
+        L.kvs_last_error.restype = ctypes.c_char_p
+        for name in EXPORTS:
+            if name not in ("kvs_decode_workspace_bytes", "kvs_last_error"):
+                getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().kvs_last_error().decode()
+
+
+def _check(rc: int) -> None:
+    if rc != KVS_OK:
+        raise KvsError(rc, last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def dtype_code(t: torch.dtype) -> int:
+    return {torch.float16: KVS_F16, torch.bfloat16: KVS_BF16}[t]
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype, device=None) -> None:
+    """Shape / dtype / layout check of a tensor handed to the library."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)} contiguous={t.is_contiguous()}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+
+
+@dataclass
+class Cache:
+    """One layer's paged KV as device tensors (the fields of kvs_paged_kv)."""
+    kv: torch.Tensor            # [num_pages][Hp][2][P][d]
+    minmax: torch.Tensor        # [num_pages][Hp][2][d]
+    page_table: torch.Tensor    # int32 [b][G][max_group_pages]
+    seq_len: torch.Tensor       # int32 [b][Hkv]
+    head_slot: torch.Tensor     # int32 [Hkv]
+    Hq: int
+
+    def struct(self) -> PagedKV:
+        num_pages, Hp, two, P, d = self.kv.shape
+        b, G, maxpg = self.page_table.shape
+        Hkv = self.seq_len.shape[1]
+        dev = self.kv.device
+        _need(self.kv, "kv", (num_pages, Hp, 2, P, d), self.kv.dtype, dev)
+        _need(self.minmax, "minmax", (num_pages, Hp, 2, d), self.kv.dtype, dev)
+        _need(self.page_table, "page_table", (b, Hkv // Hp, maxpg), torch.int32, dev)
+        _need(self.seq_len, "seq_len", (b, Hkv), torch.int32, dev)
+        _need(self.head_slot, "head_slot", (Hkv,), torch.int32, dev)
+        return PagedKV(self.kv.data_ptr(), self.minmax.data_ptr(), self.page_table.data_ptr(),
+                       self.seq_len.data_ptr(), self.head_slot.data_ptr(), b, self.Hq, Hkv, Hp,
+                       d, P, maxpg, num_pages, dtype_code(self.kv.dtype))
+
+
+def kvs_build_minmax(cache: Cache, stream=None) -> None:
+    s = cache.struct()
+    _check(lib().kvs_build_minmax(ctypes.byref(s), _stream(stream)))
+
+
+def kvs_score_pages(cache: Cache, q: torch.Tensor, scores: torch.Tensor, stream=None) -> None:
+    s = cache.struct()
+    _need(q, "q", (s.b, s.Hq, s.d), cache.kv.dtype, cache.kv.device)
+    _need(scores, "scores", (s.b, s.Hkv, s.max_group_pages), torch.float32, cache.kv.device)
+    _check(lib().kvs_score_pages(ctypes.byref(s), _ptr(q), _ptr(scores), _stream(stream)))
+
+
+def kvs_topk_pages(scores: torch.Tensor, seq_len: torch.Tensor, P: int, K: int,
+                   sel: torch.Tensor, sel_count: torch.Tensor, stream=None) -> None:
+    b, Hkv, max_pages = scores.shape
+    _need(scores, "scores", (b, Hkv, max_pages), torch.float32)
+    _need(seq_len, "seq_len", (b, Hkv), torch.int32, scores.device)
+    _need(sel, "sel", (b, Hkv, K), torch.int32, scores.device)
+    _need(sel_count, "sel_count", (b, Hkv), torch.int32, scores.device)
+    _check(lib().kvs_topk_pages(_ptr(scores), _ptr(seq_len), P, b, Hkv, max_pages, K, _ptr(sel),
+                                _ptr(sel_count), _stream(stream)))
+
+
+def kvs_plan_split(budgets: np.ndarray, head_slot: np.ndarray, Hp: int, cap: float,
+                   T: int) -> np.ndarray:
+    B = np.ascontiguousarray(budgets, dtype=np.float64)
+    hs = np.ascontiguousarray(head_slot, dtype=np.int32)
+    L, Hkv = B.shape
+    S = np.zeros((L, Hkv // Hp), dtype=np.int32)
+    _check(lib().kvs_plan_split(B.ctypes.data, hs.ctypes.data, L, Hkv, Hp, float(cap), int(T),
+                                S.ctypes.data))
+    return S
+
+
+def kvs_cluster_heads(budgets: np.ndarray, Hp: int) -> np.ndarray:
+    B = np.ascontiguousarray(budgets, dtype=np.float64)
+    L, Hkv = B.shape
+    hs = np.zeros((L, Hkv), dtype=np.int32)
+    _check(lib().kvs_cluster_heads(B.ctypes.data, L, Hkv, Hp, hs.ctypes.data))
+    return hs
+
+
+def kvs_decode_workspace_bytes(b: int, Hq: int, d: int, S_row: Sequence[int]) -> int:
+    S = np.ascontiguousarray(S_row, dtype=np.int32)
+    return int(lib().kvs_decode_workspace_bytes(b, Hq, d, S.ctypes.data, len(S)))
+
+
+def kvs_decode_attn(cache: Cache, q: torch.Tensor, sel: Optional[torch.Tensor],
+                    sel_count: Optional[torch.Tensor], K: int, S_row: Sequence[int], scale: float,
+                    workspace: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    s = cache.struct()
+    dev = cache.kv.device
+    _need(q, "q", (s.b, s.Hq, s.d), cache.kv.dtype, dev)
+    _need(out, "out", (s.b, s.Hq, s.d), torch.float32, dev)
+    if sel is not None:
+        _need(sel, "sel", (s.b, s.Hkv, K), torch.int32, dev)
+        _need(sel_count, "sel_count", (s.b, s.Hkv), torch.int32, dev)
+    if not workspace.is_contiguous() or workspace.device != dev:
+        raise ValueError("workspace must be a contiguous tensor on the cache's device")
+    S = np.ascontiguousarray(S_row, dtype=np.int32)
+    if S.shape != (s.Hkv // s.Hp,):
+        raise ValueError(f"S_row must have one entry per group ({s.Hkv // s.Hp})")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib().kvs_decode_attn(ctypes.byref(s), _ptr(q), _ptr(sel), _ptr(sel_count), int(K),
+                                 S.ctypes.data, float(scale), _ptr(workspace), nbytes, _ptr(out),
+                                 _stream(stream)))
+
+
+def kvs_decode_concurrency(device: int, d: int, gqa: int, dtype: torch.dtype) -> int:
+    W = ctypes.c_int32(0)
+    _check(lib().kvs_decode_concurrency(device, d, gqa, dtype_code(dtype), ctypes.byref(W)))
+    return W.value

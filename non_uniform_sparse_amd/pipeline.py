@@ -1,0 +1,116 @@
+"""One decode step over every layer of a workload, on one GPU.
+
+Set-up (once): cluster heads by budget, build the ragged caches and their
+min-max metadata, plan the static split map, allocate the step's buffers.
+Step: for each layer, [score pages -> top-K pages ->] split-K decode +
+combine, all launched on one stream with no host synchronisation; the grid
+of every launch comes from the static split map, never from the data.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+from . import kvs
+from .layout import RaggedLayout, build_caches
+from .workloads import Workload, torch_dtype
+
+__all__ = ["DecodeStep", "splits_per_request", "topk_cap"]
+
+
+def splits_per_request(W: int, b: int, G: int, mean_units: float, min_units: int = 8) -> int:
+    """Splits T of one request's layer: enough workgroups to fill the chip
+    (W concurrent, shared by b requests), but no split smaller than about
+    ``min_units`` pages and never fewer than one split per group."""
+    t = W // max(1, b)
+    t = min(t, max(1, math.ceil(mean_units / min_units)))
+    return max(G, t)
+
+
+def topk_cap(wl: Workload) -> float:
+    """Budget cap for the split weights when a top-K also bounds the work:
+    a head never attends more than K*P tokens, i.e. a budget of K*P / N."""
+    c = wl.cfg
+    if not c.topk:
+        return 0.0
+    return min(1.0, c.topk * c.P / float(wl.contexts.mean()))
+
+
+@dataclass
+class LayerBuffers:
+    scores: Optional[torch.Tensor]
+    sel: Optional[torch.Tensor]
+    sel_count: Optional[torch.Tensor]
+    out: torch.Tensor
+
+
+class DecodeStep:
+    def __init__(self, wl: Workload, device="cuda", T: Optional[int] = None,
+                 head_slot: Optional[np.ndarray] = None, S: Optional[np.ndarray] = None,
+                 poison: bool = True):
+        c = wl.cfg
+        self.wl, self.cfg, self.device = wl, c, device
+        if head_slot is None:
+            head_slot = (kvs.kvs_cluster_heads(wl.budgets, c.Hp) if c.clustered else
+                         np.tile(np.arange(c.Hkv, dtype=np.int32), (c.L, 1)))
+        self.head_slot = np.asarray(head_slot, dtype=np.int32)
+        self.caches, self.layouts = build_caches(wl, self.head_slot, device=device, poison=poison)
+        for cache in self.caches:
+            kvs.kvs_build_minmax(cache)
+        dt = torch_dtype(c.dtype)
+        self.W = kvs.kvs_decode_concurrency(torch.device(device).index or 0, c.d, c.Gq, dt)
+        if S is None:
+            if T is None:
+                if c.topk:
+                    units = float(np.minimum(c.topk, -(-wl.n // c.P)).sum(axis=2).mean())
+                else:
+                    units = float((-(-wl.n // c.P)).sum(axis=2).mean())
+                T = splits_per_request(self.W, c.b, c.G, units)
+            S = kvs.kvs_plan_split(wl.budgets, self.head_slot, c.Hp, topk_cap(wl), T)
+        self.S = np.asarray(S, dtype=np.int32)
+        self.T = int(self.S[0].sum())
+        self.scale = 1.0 / math.sqrt(c.d)
+        ws = max(kvs.kvs_decode_workspace_bytes(c.b, c.Hq, c.d, row) for row in self.S)
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
+        self.bufs: List[LayerBuffers] = []
+        for l in range(c.L):
+            maxpg = self.layouts[l].page_table.shape[2]
+            if c.topk:
+                scores = torch.empty((c.b, c.Hkv, maxpg), dtype=torch.float32, device=device)
+                sel = torch.empty((c.b, c.Hkv, c.topk), dtype=torch.int32, device=device)
+                cnt = torch.empty((c.b, c.Hkv), dtype=torch.int32, device=device)
+            else:
+                scores = sel = cnt = None
+            out = torch.empty((c.b, c.Hq, c.d), dtype=torch.float32, device=device)
+            self.bufs.append(LayerBuffers(scores, sel, cnt, out))
+
+    def queries(self) -> List[torch.Tensor]:
+        return [self.wl.q(l, device=self.device) for l in range(self.cfg.L)]
+
+    # ------------------------------------------------------------- per step --
+    def select(self, l: int, q: torch.Tensor, stream=None) -> None:
+        """Score every page of layer l and keep each head's top-K."""
+        c, cache, buf = self.cfg, self.caches[l], self.bufs[l]
+        kvs.kvs_score_pages(cache, q, buf.scores, stream)
+        kvs.kvs_topk_pages(buf.scores, cache.seq_len, c.P, c.topk, buf.sel, buf.sel_count, stream)
+
+    def attend(self, l: int, q: torch.Tensor, stream=None, S_row=None) -> torch.Tensor:
+        c, buf = self.cfg, self.bufs[l]
+        kvs.kvs_decode_attn(self.caches[l], q, buf.sel, buf.sel_count, c.topk or 0,
+                            self.S[l] if S_row is None else S_row, self.scale, self.workspace,
+                            buf.out, stream)
+        return buf.out
+
+    def run_layer(self, l: int, q: torch.Tensor, stream=None) -> torch.Tensor:
+        if self.cfg.topk:
+            self.select(l, q, stream)
+        return self.attend(l, q, stream)
+
+    def run(self, qs: List[torch.Tensor], stream=None) -> None:
+        for l in range(self.cfg.L):
+            self.run_layer(l, qs[l], stream)

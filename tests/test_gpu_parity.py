@@ -1,0 +1,142 @@
+"""GPU parity of the whole decode path against the fp64 oracle, through the
+C ABI, on the five workloads (the two largest on seeded samples of requests
+and layers, with the caches built at full size and the split map the bench
+uses) and on edge cases."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_harness import Stats, assert_output_bar, check_layer, require_gpu, say
+from non_uniform_sparse_amd import kvs
+from non_uniform_sparse_amd.pipeline import DecodeStep
+from non_uniform_sparse_amd.workloads import make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _full(name, **ov):
+    require_gpu()
+    wl = make_workload(name, **ov)
+    say(f"[case] {name} {ov} building caches")
+    step = DecodeStep(wl, device="cuda")
+    say(f"[case] {name}: W={step.W} T={step.T} S[0]={step.S[0].tolist()}")
+    return wl, step
+
+
+@pytest.mark.parametrize("name", ["tiny_ragged", "llama8b_ragged", "flexicache_topk"])
+def test_workload_full(name):
+    wl, step = _full(name)
+    st = Stats()
+    qs = step.queries()
+    for l in range(wl.cfg.L):
+        check_layer(step, l, qs[l], range(wl.cfg.b), st)
+    assert_output_bar(st, name)
+
+
+@pytest.mark.parametrize("name,requests,layers", [
+    ("longctx_skew", [0, 3], [0, 1, 16, 31]),
+    ("gemma3_mixed", [0, 1, 32, 63], [0, 9, 24, 47]),
+])
+def test_workload_sampled(name, requests, layers):
+    wl, step = _full(name)
+    st = Stats()
+    qs = step.queries()
+    step.run(qs)                       # every layer runs, as in the bench
+    torch.cuda.synchronize()
+    for l in layers:
+        check_layer(step, l, qs[l], requests, st)
+    assert_output_bar(st, name)
+
+
+def _split_rows(step, l):
+    c = step.cfg
+    T = int(step.S[l].sum())
+    uniform = kvs.kvs_plan_split(np.ones((1, c.Hkv)), step.head_slot[l:l + 1], c.Hp, 0.0, T)[0]
+    return {"planned": step.S[l], "uniform": uniform, "one": np.ones(c.G, dtype=np.int32),
+            "many": np.full(c.G, 997, dtype=np.int32)}
+
+
+@pytest.mark.parametrize("name", ["tiny_ragged", "flexicache_topk"])
+def test_split_invariance(name):
+    """The combined output does not depend on the split map."""
+    wl, step = _full(name, **({"b": 6} if name == "flexicache_topk" else {}))
+    q = step.queries()[0]
+    if wl.cfg.topk:
+        step.select(0, q)
+    outs = {}
+    c = wl.cfg
+    for key, row in _split_rows(step, 0).items():
+        need = kvs.kvs_decode_workspace_bytes(c.b, c.Hq, c.d, row)
+        if need > step.workspace.numel():
+            step.workspace = torch.empty(need, dtype=torch.uint8, device="cuda")
+        outs[key] = step.attend(0, q, S_row=row).clone()
+    torch.cuda.synchronize()
+    for key, o in outs.items():
+        diff = (o - outs["planned"]).abs().max().item()
+        say(f"split {key}: max diff vs planned {diff:.2e}")
+        assert diff <= 1e-5
+
+
+def test_full_topk_equals_dense():
+    """With K at least every head's page count, top-K attention is dense
+    attention over all retained tokens -- bit for bit, since the selected
+    list is every page in ascending order."""
+    require_gpu()
+    wl = make_workload("llama8b_ragged", b=3, N=1000)
+    step = DecodeStep(wl, device="cuda")
+    c = wl.cfg
+    q = step.queries()[0]
+    dense = step.attend(0, q).clone()
+    cache = step.caches[0]
+    maxpg = step.layouts[0].page_table.shape[2]
+    scores = torch.empty((c.b, c.Hkv, maxpg), dtype=torch.float32, device="cuda")
+    K = maxpg + 5
+    sel = torch.empty((c.b, c.Hkv, K), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((c.b, c.Hkv), dtype=torch.int32, device="cuda")
+    kvs.kvs_score_pages(cache, q, scores)
+    kvs.kvs_topk_pages(scores, cache.seq_len, c.P, K, sel, cnt)
+    out = torch.empty_like(dense)
+    kvs.kvs_decode_attn(cache, q, sel, cnt, K, step.S[0], step.scale, step.workspace, out)
+    torch.cuda.synchronize()
+    npg = (cache.seq_len + 15) // 16
+    assert torch.equal(cnt, npg)
+    assert torch.equal(out, dense)
+
+
+@pytest.mark.parametrize("Hp,d,Hq,dtype,n_list", [
+    (4, 128, 32, "f16", [1, 16, 17, 31, 32, 33, 200, 5]),
+    (1, 128, 16, "bf16", [1, 2, 15, 16, 64, 65, 300, 7]),
+    (8, 256, 16, "bf16", [3, 16, 48, 49, 100, 1, 129, 40]),
+    (2, 256, 64, "f16", [16, 1, 77, 90, 33, 18, 250, 2]),
+    (4, 128, 8, "bf16", [40, 1, 16, 300, 64, 65, 17, 2]),
+])
+@pytest.mark.parametrize("topk", [None, 3])
+def test_edge_cases(Hp, d, Hq, dtype, n_list, topk):
+    """Single-token heads, page-boundary lengths, partial pages, every GQA
+    width the kernels build, group sizes 1..8, K above and below the page
+    counts, and split maps with more splits than units (empty splits)."""
+    require_gpu()
+    wl = make_workload("llama8b_ragged", b=2, N=400, Hq=Hq, d=d, dtype=dtype, Hp=Hp, topk=topk)
+    wl.n[0, 0, :] = n_list
+    wl.n[1, 0, :] = n_list[::-1]
+    say(f"[case] edge Hp={Hp} d={d} Hq={Hq} {dtype} topk={topk} n={n_list}")
+    c = wl.cfg
+    for T in (c.G, c.G + 3, 64):
+        step = DecodeStep(wl, device="cuda", T=T)
+        st = Stats()
+        check_layer(step, 0, step.queries()[0], range(c.b), st)
+        assert_output_bar(st, f"edge T={T}")
+
+
+def test_deterministic():
+    wl, step = _full("flexicache_topk", b=4)
+    q = step.queries()[0]
+    a = step.run_layer(0, q).clone()
+    sel_a = step.bufs[0].sel.clone()
+    b = step.run_layer(0, q).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(sel_a, step.bufs[0].sel)

@@ -1,0 +1,205 @@
+"""Host logic: ragged layout round trip, C-ABI exports, argument
+validation (checked before any HIP call, so no GPU is needed) and the host
+planner / clustering against the oracle."""
+
+import ctypes
+import math
+import re
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from non_uniform_sparse_amd import kvs
+from non_uniform_sparse_amd.layout import build_caches, unpack_head
+from non_uniform_sparse_amd.workloads import make_workload
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    if not os.path.exists(kvs.LIB_PATH):
+        pytest.skip("libkvs.so not built")
+    return kvs.lib()
+
+
+def test_header_symbols_exported():
+    L = _lib()
+    header = open(os.path.join(ROOT, "include", "kvs.h")).read()
+    declared = set(re.findall(r"\b(kvs_[a-z_]+)\s*\(", header))
+    assert declared == set(kvs.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_last_error_starts_empty_and_reports():
+    _lib()
+    with pytest.raises(kvs.KvsError) as e:
+        kvs.kvs_plan_split(np.ones((1, 8)), np.zeros((1, 8), dtype=np.int32), 4, 0.0, 4)
+    assert e.value.code == kvs.KVS_EINVAL and "permutation" in str(e.value)
+
+
+@pytest.mark.parametrize("name,overrides", [
+    ("tiny_ragged", {}),
+    ("llama8b_ragged", dict(b=2, N=700)),
+    ("flexicache_topk", dict(b=2, N=320)),
+    ("gemma3_mixed", dict(b=2, L=10, N=3000)),
+])
+def test_layout_round_trip(name, overrides):
+    wl = make_workload(name, **overrides)
+    c = wl.cfg
+    hs = np.stack([O.cluster_heads(wl.budgets[l], c.Hp) if c.clustered else np.arange(c.Hkv)
+                   for l in range(c.L)])
+    caches, layouts = build_caches(wl, hs, device="cpu")
+    for l in range(c.L):
+        lay = layouts[l]
+        for r in range(c.b):
+            for i in range(c.G):
+                members = [h for h in range(c.Hkv) if hs[l, h] // c.Hp == i]
+                k = O.group_page_count([wl.n[r, l, h] for h in members], c.P)
+                row = lay.page_table[r, i]
+                assert (row[:k] >= 0).all() and (row[k:] == -1).all()
+            for h in range(c.Hkv):
+                K, V = unpack_head(caches[l].kv, lay, r, h, c.P)
+                K0, V0 = wl.head_kv(r, l, h, int(hs[l, h]))
+                assert torch.equal(K, K0) and torch.equal(V, V0)
+    # physical ids are distinct within a pool
+    for lam in range(c.nbanks):
+        ls = [l for l in range(c.L) if layouts[l].pool == lam]
+        for r in range(c.b):
+            used = np.concatenate([layouts[ls[0]].page_table[r, i][layouts[ls[0]].page_table[r, i] >= 0]
+                                   for i in range(c.G)])
+            assert len(np.unique(used)) == len(used)
+
+
+# ------------------------------------------------------------- planner -------
+
+@pytest.mark.parametrize("seed", range(3))
+def test_cluster_heads_matches_oracle(seed):
+    _lib()
+    rng = np.random.default_rng(seed)
+    B = rng.uniform(0.02, 1.0, (6, 8))
+    B[0, 3] = B[0, 5]                        # a tie
+    B[1] = 0.5                               # all equal
+    got = kvs.kvs_cluster_heads(B, 4)
+    for l in range(6):
+        assert got[l].tolist() == O.cluster_heads(B[l], 4).tolist()
+
+
+def test_plan_split_matches_oracle_random():
+    _lib()
+    rng = np.random.default_rng(0)
+    for _ in range(2000):
+        Hp = int(rng.choice([1, 2, 4]))
+        G = int(rng.integers(1, 5))
+        Hkv = Hp * G
+        L = int(rng.integers(1, 3))
+        B = rng.uniform(1e-6, 1.0, (L, Hkv))
+        if rng.random() < 0.3:
+            B = np.round(B * 4) / 4 + 0.25      # many equal loads
+            B = np.minimum(B, 1.0)
+        hs = np.stack([rng.permutation(Hkv) for _ in range(L)])
+        T = int(rng.integers(G, 70))
+        cap = float(rng.choice([0.0, 0.1, 0.37]))
+        got = kvs.kvs_plan_split(B, hs, Hp, cap, T)
+        want = O.plan_split(B, hs, Hp, cap, T)
+        assert got.tolist() == want.tolist()
+
+
+@pytest.mark.parametrize("name", ["tiny_ragged", "llama8b_ragged", "flexicache_topk",
+                                  "longctx_skew", "gemma3_mixed"])
+def test_plan_split_matches_oracle_on_workloads(name):
+    _lib()
+    wl = make_workload(name)
+    c = wl.cfg
+    hs = kvs.kvs_cluster_heads(wl.budgets, c.Hp) if c.clustered else \
+        np.tile(np.arange(c.Hkv, dtype=np.int32), (c.L, 1))
+    cap = c.topk * c.P / float(wl.contexts.mean()) if c.topk else 0.0
+    for T in (c.G, 7, 64, 1024):
+        T = max(T, c.G)
+        assert kvs.kvs_plan_split(wl.budgets, hs, c.Hp, cap, T).tolist() == \
+            O.plan_split(wl.budgets, hs, c.Hp, cap, T).tolist()
+
+
+# --------------------------------------------------------- validation --------
+
+class _FakeCache:
+    """A descriptor with fake (never dereferenced) device pointers."""
+
+    def __init__(self, **kw):
+        f = dict(kv=0x10000, minmax=0x20000, page_table=0x30000, seq_len=0x40000,
+                 head_slot=0x50000, b=1, Hq=32, Hkv=8, Hp=4, d=128, P=16,
+                 max_group_pages=4, num_pages=8, dtype=kvs.KVS_F16)
+        f.update(kw)
+        self.s = kvs.PagedKV(**f)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kv=0), kvs.KVS_EINVAL),
+    (dict(kv=0x10008), kvs.KVS_EINVAL),       # misaligned
+    (dict(Hq=30), kvs.KVS_EINVAL),
+    (dict(Hp=3), kvs.KVS_EINVAL),
+    (dict(d=64), kvs.KVS_EUNSUPPORTED),
+    (dict(P=32), kvs.KVS_EUNSUPPORTED),
+    (dict(dtype=7), kvs.KVS_EUNSUPPORTED),
+    (dict(Hq=24), kvs.KVS_EUNSUPPORTED),      # query group of 3
+    (dict(b=0), kvs.KVS_EINVAL),
+])
+def test_validation_before_launch(kw, code):
+    L = _lib()
+    s = _FakeCache(**kw).s
+    assert L.kvs_build_minmax(ctypes.byref(s), None) == code
+    assert kvs.last_error()
+    assert L.kvs_score_pages(ctypes.byref(s), 0x60000, 0x70000, None) == code
+
+
+def test_decode_validation():
+    L = _lib()
+    s = _FakeCache().s
+    S = np.array([2, 2], dtype=np.int32)
+    need = kvs.kvs_decode_workspace_bytes(1, 32, 128, S)
+    assert need == 1 * 32 * 2 * 128 * 4 + 256
+    args = lambda **k: [ctypes.byref(s), k.get("q", 0x60000), k.get("sel", None), k.get("cnt", None),
+                        k.get("K", 0), k.get("S", S).ctypes.data, ctypes.c_float(k.get("scale", 0.088)),
+                        k.get("ws", 0x100000), k.get("wsb", need), k.get("out", 0x80000), None]
+    assert L.kvs_decode_attn(*args(wsb=need - 1)) == kvs.KVS_ENOSPC
+    assert L.kvs_decode_attn(*args(S=np.array([2, 0], dtype=np.int32))) == kvs.KVS_EINVAL
+    assert L.kvs_decode_attn(*args(sel=0x90000, cnt=None, K=4)) == kvs.KVS_EINVAL
+    assert L.kvs_decode_attn(*args(sel=0x90000, cnt=0xA0000, K=0)) == kvs.KVS_EINVAL
+    assert L.kvs_decode_attn(*args(scale=-1.0)) == kvs.KVS_EINVAL
+    assert L.kvs_decode_attn(*args(ws=0x100010)) == kvs.KVS_EINVAL   # workspace alignment
+    assert L.kvs_decode_attn(*args(q=0)) == kvs.KVS_EINVAL
+
+
+def test_topk_validation():
+    L = _lib()
+    ok = [0x1000, 0x2000, 16, 1, 8, 640, 64, 0x3000, 0x4000, None]
+    bad = {7: 0, 2: 32, 5: 9000}
+    for idx, val in bad.items():
+        a = list(ok)
+        a[idx - 1 if idx == 7 else idx] = val
+    a = list(ok); a[6] = 0
+    assert L.kvs_topk_pages(*a) == kvs.KVS_EINVAL
+    a = list(ok); a[6] = 2000
+    assert L.kvs_topk_pages(*a) == kvs.KVS_EINVAL
+    a = list(ok); a[2] = 32
+    assert L.kvs_topk_pages(*a) == kvs.KVS_EUNSUPPORTED
+    a = list(ok); a[5] = 9000
+    assert L.kvs_topk_pages(*a) == kvs.KVS_EUNSUPPORTED
+    a = list(ok); a[0] = None
+    assert L.kvs_topk_pages(*a) == kvs.KVS_EINVAL
+
+
+def test_plan_validation():
+    _lib()
+    hs = np.tile(np.arange(8, dtype=np.int32), (1, 1))
+    with pytest.raises(kvs.KvsError):
+        kvs.kvs_plan_split(np.ones((1, 8)), hs, 4, 0.0, 1)          # T < G
+    with pytest.raises(kvs.KvsError):
+        kvs.kvs_plan_split(np.zeros((1, 8)), hs, 4, 0.0, 4)         # budget 0
+    with pytest.raises(kvs.KvsError):
+        kvs.kvs_plan_split(np.ones((1, 8)), hs, 3, 0.0, 4)          # Hkv % Hp
+    with pytest.raises(kvs.KvsError):
+        kvs.kvs_cluster_heads(np.full((1, 8), 1.5), 4)
