@@ -1,0 +1,241 @@
+"""Decode-attention benchmark on one MI355X.
+
+A step is one full decode step of the workload: for every layer, page
+scores -> top-K pages (top-K workloads only) -> ragged split-K decode + LSE
+combine, all on one stream.  Inputs (caches, min-max metadata, queries) are
+resident in HBM before the timed region starts.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from non_uniform_sparse_amd import kvs  # noqa: E402
+from non_uniform_sparse_amd.pipeline import DecodeStep  # noqa: E402
+from non_uniform_sparse_amd.workloads import CONFIGS, make_workload  # noqa: E402
+
+METRIC = "decode-attn KV GB/s (% of HBM peak) + µs/step, ragged top-K, 1 MI355X"
+HBM_PEAK_GBPS = 8000.0
+DEFAULT_CONFIG = "gemma3_mixed"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(step: DecodeStep, l: int) -> dict:
+    """Bytes the method itself must move in layer l (not the dense work it
+    avoids).  KV: 2*d*s per valid token of every attended page.  Metadata:
+    2*d*s per valid page (top-K only).  Small terms: q, scores, selection,
+    split partials (written + read) and the output."""
+    c, wl = step.cfg, step.wl
+    s = 2
+    n = wl.n[:, l, :]                                       # [b][Hkv]
+    npg = -(-n // c.P)
+    if c.topk:
+        sel = step.bufs[l].sel.cpu().numpy()
+        cnt = step.bufs[l].sel_count.cpu().numpy()
+        toks = 0
+        for r in range(c.b):
+            for h in range(c.Hkv):
+                pages = sel[r, h, :cnt[r, h]]
+                last = npg[r, h] - 1
+                full = int((pages != last).sum())
+                toks += full * c.P + (int(n[r, h] - last * c.P) if (pages == last).any() else 0)
+        units = int(cnt.sum())
+    else:
+        toks = int(n.sum())
+        units = int(npg.sum())
+    kv = toks * 2 * c.d * s
+    meta = int(npg.sum()) * 2 * c.d * s if c.topk else 0
+    # partials: one row per (r, query head, split touching its head); bounded by
+    # (splits + heads per group) * Gq per (r, group)
+    rows = c.b * (int(step.S[l].sum()) + c.Hkv) * c.Gq
+    small = (c.b * c.Hq * c.d * s * (2 if c.topk else 1)
+             + (c.b * c.Hkv * step.layouts[l].page_table.shape[2] * 4 * 2 if c.topk else 0)
+             + (c.b * c.Hkv * c.topk * 4 * 2 if c.topk else 0)
+             + rows * (c.d + 1) * 4 * 2
+             + c.b * c.Hq * c.d * 4)
+    return {"kv": kv, "meta": meta, "small": small, "tokens": toks, "units": units,
+            "decode_launch": kv + rows * (c.d + 1) * 4 * 2 + c.b * c.Hq * c.d * (s + 4)}
+
+
+def cpu_baseline(wl, step, budget_s: float = 12.0) -> dict:
+    """The fp64 oracle timed on this host on a bounded sample of the same
+    workload: whole heads (score + top-K + attention; min-max metadata
+    precomputed, as on the GPU), until ~budget_s of work."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    c = wl.cfg
+    q = [wl.q(l, device=step.device).double().cpu().numpy() for l in range(min(c.L, 4))]
+    scale = 1.0 / math.sqrt(c.d)
+    done_bytes, spent, heads = 0, 0.0, 0
+    order = [(r, l, h) for l in range(min(c.L, 4)) for r in range(c.b) for h in range(c.Hkv)]
+    for r, l, h in order:
+        pos = int(step.head_slot[l, h])
+        K, V = wl.head_kv(r, l, h, pos, device=step.device)
+        K, V = K.double().cpu().numpy(), V.double().cpu().numpy()
+        lo, hi = O.page_minmax(K, c.P)
+        qg = q[l][r, h * c.Gq:(h + 1) * c.Gq]
+        t0 = time.perf_counter()
+        if c.topk:
+            pages = O.topk_pages(O.page_scores(qg, lo, hi), c.topk)
+        else:
+            pages = np.arange(lo.shape[0])
+        O.decode_head(qg, K, V, pages, c.P, scale)
+        spent += time.perf_counter() - t0
+        n = K.shape[0]
+        toks = sum(min(c.P, n - int(p) * c.P) for p in pages)
+        done_bytes += toks * 2 * c.d * 2
+        heads += 1
+        if spent >= budget_s:
+            break
+    return {"value": done_bytes / spent / 1e9, "unit": "GB/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{heads} whole heads (request-major from layer 0) of {c.name}, "
+                      f"{done_bytes / 1e6:.1f} MB of KV in {spent:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the decode path here runs on a single MI355X "
+              "(see DESIGN.md for how it would shard); run with --gpus 1", file=sys.stderr)
+        return 2
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    t0 = time.time()
+    wl = make_workload(args.config)
+    c = wl.cfg
+    step = DecodeStep(wl, device=dev)
+    qs = step.queries()
+    torch.cuda.synchronize()
+    log(f"[bench] {c.name}: set-up {time.time() - t0:.1f} s, W={step.W}, T={step.T}, "
+        f"S[0]={step.S[0].tolist()}")
+
+    stream = torch.cuda.Stream()
+    # Small working sets are flushed from L2 / MALL before each step.
+    flush = None
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step.run(qs, stream)
+    stream.synchronize()
+    ab = [algorithmic_bytes(step, l) for l in range(c.L)]
+    kv_bytes = sum(a["kv"] for a in ab)
+    path_bytes = sum(a["kv"] + a["meta"] + a["small"] for a in ab)
+    if path_bytes < 8e9:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    kern = {"score": [], "topk": [], "decode_attn": []}
+    step_ms = []
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for _ in range(args.steps):
+        if flush is not None:
+            with torch.cuda.stream(stream):
+                flush.zero_()
+        s0, s1 = ev(), ev()
+        s0.record(stream)
+        marks = []
+        for l in range(c.L):
+            q = qs[l]
+            if c.topk:
+                a, b_, d_ = ev(), ev(), ev()
+                a.record(stream)
+                kvs.kvs_score_pages(step.caches[l], q, step.bufs[l].scores, stream)
+                b_.record(stream)
+                kvs.kvs_topk_pages(step.bufs[l].scores, step.caches[l].seq_len, c.P, c.topk,
+                                   step.bufs[l].sel, step.bufs[l].sel_count, stream)
+                d_.record(stream)
+                marks.append(("score", a, b_))
+                marks.append(("topk", b_, d_))
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            step.attend(l, q, stream)
+            e1.record(stream)
+            marks.append(("decode_attn", e0, e1))
+        s1.record(stream)
+        stream.synchronize()
+        step_ms.append(s0.elapsed_time(s1))
+        for k, a, b_ in marks:
+            kern[k].append(a.elapsed_time(b_))
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - wall0) * 1e3
+
+    ms = statistics.mean(step_ms) if flush is not None else wall_ms / args.steps
+    dec_ms = statistics.mean(kern["decode_attn"])
+    dec_bytes = statistics.mean(a["decode_launch"] for a in ab)
+    achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
+    value = kv_bytes / (ms * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "us_per_step": round(ms * 1e3, 1),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "path_GBps": round(path_bytes / (ms * 1e-3) / 1e9, 1),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": c.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": c.name, "requests": c.b, "layers": c.L, "q_heads": c.Hq,
+            "kv_heads": c.Hkv, "head_dim": c.d, "page": c.P, "Hp": c.Hp,
+            "topk_pages": c.topk, "splits_per_request": step.T,
+            "kv_bytes_per_step": kv_bytes, "path_bytes_per_step": path_bytes,
+            "cache_flush_between_steps": flush is not None,
+        },
+        "kernels_ms_avg": {k: round(statistics.mean(v), 5) for k, v in kern.items() if v},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "kvs_decode_attn (split-K decode + combine)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+        },
+        "wall_ms_per_step_incl_flush": round(wall_ms / args.steps, 4),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host ...")
+        rec["cpu_baseline"] = cpu_baseline(wl, step, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
