@@ -16,46 +16,46 @@ LIB = os.path.join(PKG, "libkvs.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-COMMON = [
-    "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
-    f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
-]
+COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function"]
 # gfx950 device code; packed-fp32 instructions are switched off.
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-munsafe-fp-atomics"]
 
 
-def sources():
-    return sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
+def sources(csrc: str = CSRC):
+    return sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, src + ".o")
-    path = os.path.join(CSRC, src)
+def _compile(src: str, csrc: str = CSRC, build_dir: str = BUILD) -> str:
+    obj = os.path.join(build_dir, src + ".o")
+    path = os.path.join(csrc, src)
+    flags = [f"-I{os.path.join(ROOT, 'include')}", f"-I{csrc}", *COMMON]
     if src.endswith(".hip"):
-        cmd = [HIPCC, "-x", "hip", *DEVICE, *COMMON, "-c", path, "-o", obj]
+        cmd = [HIPCC, "-x", "hip", *DEVICE, *flags, "-c", path, "-o", obj]
     else:  # host-only C++
-        cmd = [HIPCC, *COMMON, "-c", path, "-o", obj]
+        cmd = [HIPCC, *flags, "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
+def build(verbose: bool = False, csrc: str = CSRC, lib: str = LIB,
+          build_dir: str = BUILD) -> str:
+    """Compile every source under ``csrc`` and link ``lib``."""
+    os.makedirs(build_dir, exist_ok=True)
+    srcs = sources(csrc)
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda f: _compile(f, csrc, build_dir), srcs))
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":

@@ -20,6 +20,8 @@
 // (d=256) K and V tiles stream in fully coalesced 16-byte accesses.  Logits
 // are pair-dots of q with K summed over the row's COLS lanes; p*V is
 // accumulated per lane and reduced over the row groups once per head.
+#include <utility>
+
 #include "kvs_device.h"
 
 namespace kvs {
@@ -67,11 +69,62 @@ __device__ void group_units(const DecodeArgs& a, int r, int gi, GroupUnits* gu) 
   __syncthreads();
 }
 
+// ---------------------------------------------------------------------------
+// Per-page math.  Logits of the page's 16 tokens against the GQ query heads
+// form a small dense contraction, S^T[16 tokens][16 cols] = K[16][d] Q^T[d][16]
+// (cols >= GQ are zero), done as d/32 v_mfma_f32_16x16x32 steps.  MFMA lane
+// layouts (gfx950): A operand lane l holds A[l%16][8(l/16)..+8] of each 32-wide
+// k block, B operand B[8(l/16)..+8][l%16], result D[4(l/16)+i][l%16], i < 4.
+// MFMA row m is mapped to token tau(m) so that the result lands where the p*V
+// step needs it: the V side gives lane l the channels 8*(l % COLS)..+8 of rows
+// rg + RPL*k (rg = l / COLS, k < TL), and the result lane of column g in row
+// group a = rg*A + hh (A = 4/RPL, hh < A) holds tokens rg + RPL*(4 hh + i).
+// Softmax statistics live in the result layout (each lane tracks the query
+// head of its column); probabilities and rescale factors reach the V lanes
+// through ds_swizzle row broadcasts.
+// ---------------------------------------------------------------------------
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b, f32x4_t c, F16) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma16x16x32(const uint4& a, const uint4& b, f32x4_t c, BF16) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// ds_swizzle bit-mask mode within 32-lane halves: source = (lane & and) | or.
+template <int AND, int OR>
+__device__ __forceinline__ float swz(float v) {
+  return __uint_as_float(__builtin_amdgcn_ds_swizzle(__float_as_uint(v), (OR << 5) | AND));
+}
+
+template <int D>
+struct Geometry {
+  static constexpr int COLS = D / 8;        // V lanes per row (8 channels each)
+  static constexpr int RPL = 64 / COLS;     // V row groups
+  static constexpr int TL = P / RPL;        // rows per V lane
+  static constexpr int A = 4 / RPL;         // result row groups per V row group
+  static constexpr int KB = D / 32;         // MFMA k blocks
+};
+
+// Value held by result lane (row group rg*A + HH, column G) broadcast to every
+// lane of V row group rg.
+template <int D, int HH, int G>
+__device__ __forceinline__ float from_result(float v) {
+  constexpr int A = Geometry<D>::A;
+  if constexpr (A == 1) return swz<0x10, G>(v);      // rows of 16; keep lane bit 4
+  else return swz<0x00, 16 * HH + G>(v);             // two result rows per 32-lane half
+}
+
 template <int D, int GQ, typename DT>
 __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
-  constexpr int COLS = D / 8;
-  constexpr int RPL = 64 / COLS;
-  constexpr int TL = P / RPL;
+  using Geo = Geometry<D>;
+  constexpr int COLS = Geo::COLS, RPL = Geo::RPL, TL = Geo::TL, A = Geo::A, KB = Geo::KB;
+  static_assert(GQ <= 16, "query group must fit the 16 MFMA columns");
   __shared__ GroupUnits gu;
   const CacheView& c = a.c;
   const int lane = threadIdx.x;
@@ -87,116 +140,187 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   const int u0 = (int)((int64_t)s * U / Si), u1 = (int)((int64_t)(s + 1) * U / Si);
   if (u0 >= u1) return;
 
-  const int rg = lane / COLS, col = lane % COLS;
+  // V-side role
+  const int rg = lane / COLS, vcol = lane % COLS;
+  const int v_off = rg * D + 8 * vcol;
+  // MFMA roles: operand row m = lane % 16 (a token), k sub-block kq = lane / 16
+  const int m = lane % 16, kq = lane / 16;
+  const int ka = m / 4, ki = m % 4;
+  const int k_tok = (ka / A) + RPL * (4 * (ka % A) + ki);   // token loaded as MFMA row m
+  const int k_off = k_tok * D + 8 * kq;
+  // result role: column (query head) rcol, row group ra holding 4 tokens
+  const int rcol = lane % 16, ra = lane / 16;
+  const int r_tok0 = (ra / A) + RPL * 4 * (ra % A);          // token of element i: r_tok0 + RPL*i
+
   const int32_t* pt = c.page_table + ((int64_t)r * c.G + gi) * c.maxpg;
   const uint16_t* kvb = reinterpret_cast<const uint16_t*>(c.kv);
   const uint16_t* qb = reinterpret_cast<const uint16_t*>(a.q);
 
-  for (int j = 0; j < c.Hp; ++j) {
-    const int a0 = max(u0, gu.start[j]), a1 = min(u1, gu.start[j] + gu.count[j]);
-    if (a0 >= a1) continue;
-    const int h = gu.head[j];
-    const int n = clampi(c.seq_len[r * c.Hkv + h], 0, P * c.maxpg);
-    const int32_t* srow = a.sel ? a.sel + ((int64_t)r * c.Hkv + h) * a.K : nullptr;
+  uint4 qop[KB];            // Q^T operand of the current head
+  float m_col, l_col;       // running max / partial sum of column rcol's head
+  float o[GQ][8];           // V-side accumulators
+  int cur_j = -1;
 
-    uint32_t qw[GQ][4];
+  auto begin_head = [&](int j) {
+    const int h = gu.head[j];
+    const bool has = rcol < GQ;
+    const uint16_t* qrow = qb + ((int64_t)r * c.Hq + h * GQ + (has ? rcol : 0)) * D + 8 * kq;
 #pragma unroll
-    for (int g = 0; g < GQ; ++g) {
-      const uint4 v = ld16(qb + ((int64_t)r * c.Hq + h * GQ + g) * D + 8 * col);
-      qw[g][0] = v.x;
-      qw[g][1] = v.y;
-      qw[g][2] = v.z;
-      qw[g][3] = v.w;
-    }
-    float m[GQ], l[GQ], o[GQ][8];
+    for (int kb = 0; kb < KB; ++kb) qop[kb] = has ? ld16(qrow + 32 * kb) : make_uint4(0, 0, 0, 0);
+    m_col = -__builtin_inff();
+    l_col = 0.f;
 #pragma unroll
-    for (int g = 0; g < GQ; ++g) {
-      m[g] = -__builtin_inff();
-      l[g] = 0.f;
+    for (int g = 0; g < GQ; ++g)
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[g][e] = 0.f;
-    }
-
-    for (int u = a0; u < a1; ++u) {
-      const int lp = srow ? srow[u - gu.start[j]] : u - gu.start[j];
-      if (lp < 0 || lp >= c.maxpg) continue;
-      const int phys = pt[lp];
-      if (phys < 0 || phys >= c.num_pages) continue;
-      const int valid = min(P, n - lp * P);
-      if (valid <= 0) continue;
-      const uint16_t* kt = kvb + ((int64_t)phys * c.Hp + j) * 2 * P * D;
-      const uint16_t* vt = kt + P * D;
-      uint4 kr[TL], vr[TL];
+  };
+  // Merge the row groups and write this split's partial for the head in slot j.
+  auto end_head = [&](int j) {
+    const int h = gu.head[j];
+    const float lt = across_sum<16>(l_col);   // total over the 4 result row groups
+    float lg[GQ], mg[GQ];
+    [&]<int... G>(std::integer_sequence<int, G...>) {
+      ((lg[G] = from_result<D, 0, G>(lt), mg[G] = from_result<D, 0, G>(m_col)), ...);
+    }(std::make_integer_sequence<int, GQ>{});
 #pragma unroll
-      for (int k = 0; k < TL; ++k) kr[k] = ld16(kt + (rg + RPL * k) * D + 8 * col);
-#pragma unroll
-      for (int k = 0; k < TL; ++k) vr[k] = ld16(vt + (rg + RPL * k) * D + 8 * col);
-
-      float z[TL][GQ];
-#pragma unroll
-      for (int k = 0; k < TL; ++k) {
-#pragma unroll
-        for (int g = 0; g < GQ; ++g) {
-          float acc = dot2(qw[g][0], kr[k].x, 0.f, DT());
-          acc = dot2(qw[g][1], kr[k].y, acc, DT());
-          acc = dot2(qw[g][2], kr[k].z, acc, DT());
-          acc = dot2(qw[g][3], kr[k].w, acc, DT());
-          z[k][g] = group_sum<COLS>(acc);
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < TL; ++k) {
-        const bool ok = rg + RPL * k < valid;
-#pragma unroll
-        for (int g = 0; g < GQ; ++g) z[k][g] = ok ? z[k][g] * a.scale_log2 : -__builtin_inff();
-        if (!ok) vr[k] = make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int g = 0; g < GQ; ++g) {
-        float tmax = z[0][g];
-#pragma unroll
-        for (int k = 1; k < TL; ++k) tmax = fmaxf(tmax, z[k][g]);
-        tmax = across_max<COLS>(tmax);
-        const float mnew = fmaxf(m[g], tmax);
-        const float corr = exp2f(m[g] - mnew);
-        m[g] = mnew;
-        l[g] *= corr;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[g][e] *= corr;
-#pragma unroll
-        for (int k = 0; k < TL; ++k) {
-          const float pk = exp2f(z[k][g] - mnew);
-          l[g] += pk;
-          const uint32_t w[4] = {vr[k].x, vr[k].y, vr[k].z, vr[k].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            o[g][2 * e] += pk * lo_f(w[e], DT());
-            o[g][2 * e + 1] += pk * hi_f(w[e], DT());
-          }
-        }
-      }
-    }
-
-    // Merge the row groups and write this split's partial for head h.
-#pragma unroll
-    for (int g = 0; g < GQ; ++g) {
-      l[g] = across_sum<COLS>(l[g]);
+    for (int g = 0; g < GQ; ++g)
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[g][e] = across_sum<COLS>(o[g][e]);
-    }
     if (rg == 0) {
 #pragma unroll
       for (int g = 0; g < GQ; ++g) {
         const int64_t row = ((int64_t)r * c.Hq + h * GQ + g) * a.Smax + s;
-        const bool empty = !(l[g] > 0.f);
-        const float inv = empty ? 0.f : 1.f / l[g];
-        float4* dst = reinterpret_cast<float4*>(a.o_part + row * D + 8 * col);
+        const bool empty = !(lg[g] > 0.f);
+        const float inv = empty ? 0.f : 1.f / lg[g];
+        float4* dst = reinterpret_cast<float4*>(a.o_part + row * D + 8 * vcol);
         dst[0] = make_float4(o[g][0] * inv, o[g][1] * inv, o[g][2] * inv, o[g][3] * inv);
         dst[1] = make_float4(o[g][4] * inv, o[g][5] * inv, o[g][6] * inv, o[g][7] * inv);
-        if (col == 0) a.lse_part[row] = empty ? -__builtin_inff() : m[g] + log2f(l[g]);
+        if (vcol == 0) a.lse_part[row] = empty ? -__builtin_inff() : mg[g] + log2f(lg[g]);
       }
     }
+  };
+
+  uint4 kr[KB], vr[TL];
+  for (int base = u0; base < u1; base += 64) {
+    const int nb = min(64, u1 - base);
+    // Lane t resolves unit base + t: its slot, physical page and valid rows.
+    int my_j = 0, my_phys = -1, my_valid = 0;
+    if (lane < nb) {
+      const int u = base + lane;
+      int j = 0;
+      for (int jj = 1; jj < c.Hp; ++jj)
+        if (gu.count[jj] > 0 && u >= gu.start[jj]) j = jj;
+      const int h = gu.head[j];
+      const int k = u - gu.start[j];
+      const int n = clampi(c.seq_len[r * c.Hkv + h], 0, P * c.maxpg);
+      const int lp = a.sel ? a.sel[((int64_t)r * c.Hkv + h) * a.K + k] : k;
+      if (lp >= 0 && lp < c.maxpg) {
+        const int ph = pt[lp];
+        if (ph >= 0 && ph < c.num_pages) {
+          my_phys = ph;
+          my_valid = min(P, n - lp * P);
+        }
+      }
+      my_j = j;
+    }
+    auto tile = [&](int t) {
+      const int phys = __builtin_amdgcn_readlane(my_phys, t);
+      const int j = __builtin_amdgcn_readlane(my_j, t);
+      return kvb + ((int64_t)phys * c.Hp + j) * 2 * P * D;
+    };
+    auto load_k = [&](const uint16_t* kt) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) kr[kb] = ld16(kt + k_off + 32 * kb);
+    };
+    auto load_v = [&](const uint16_t* kt) {
+#pragma unroll
+      for (int k = 0; k < TL; ++k) vr[k] = ld16(kt + P * D + v_off + RPL * k * D);
+    };
+    int next_phys = __builtin_amdgcn_readlane(my_phys, 0);
+    if (next_phys >= 0) {
+      const uint16_t* kt = tile(0);
+      load_k(kt);
+      load_v(kt);
+    }
+    for (int t = 0; t < nb; ++t) {
+      const int j = __builtin_amdgcn_readlane(my_j, t);
+      const int phys = next_phys;
+      const int valid = __builtin_amdgcn_readlane(my_valid, t);
+      next_phys = t + 1 < nb ? __builtin_amdgcn_readlane(my_phys, t + 1) : -1;
+      if (j != cur_j) {
+        if (cur_j >= 0) end_head(cur_j);
+        begin_head(j);
+        cur_j = j;
+      }
+      const uint16_t* nt = next_phys >= 0 ? tile(t + 1) : nullptr;
+      if (phys < 0 || valid <= 0) {
+        if (nt) {
+          load_k(nt);
+          load_v(nt);
+        }
+        continue;
+      }
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) acc = mfma16x16x32(kr[kb], qop[kb], acc, DT());
+      if (nt) load_k(nt);   // K consumed: fetch the next unit's K
+
+      // online softmax in the result layout (column rcol = query head)
+      float z[4], tmax = -__builtin_inff();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        z[i] = r_tok0 + RPL * i < valid ? acc[i] * a.scale_log2 : -__builtin_inff();
+        tmax = fmaxf(tmax, z[i]);
+      }
+      tmax = across_max<16>(tmax);
+      const float mnew = fmaxf(m_col, tmax);
+      const float corr = __builtin_amdgcn_exp2f(m_col - mnew);
+      m_col = mnew;
+      float pr[4], psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pr[i] = __builtin_amdgcn_exp2f(z[i] - mnew);
+        psum += pr[i];
+      }
+      l_col = l_col * corr + psum;
+
+      // broadcast rescale factors and probabilities to the V lanes
+      float cg[GQ], pb[TL][GQ];
+      [&]<int... G>(std::integer_sequence<int, G...>) {
+        ((cg[G] = from_result<D, 0, G>(corr)), ...);
+        [&]<int... HI>(std::integer_sequence<int, HI...>) {
+          auto one = [&]<int HIV>() {
+            constexpr int HH = HIV / 4, I = HIV % 4;
+            ((pb[4 * HH + I][G] = from_result<D, HH, G>(pr[I])), ...);
+          };
+          (one.template operator()<HI>(), ...);
+        }(std::make_integer_sequence<int, TL>{});
+      }(std::make_integer_sequence<int, GQ>{});
+
+#pragma unroll
+      for (int g = 0; g < GQ; ++g)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[g][e] *= cg[g];
+#pragma unroll
+      for (int k = 0; k < TL; ++k) {
+        // rows past the valid count hold no token (possibly NaN): zero them
+        const bool ok = rg + RPL * k < valid;
+        const uint32_t w[4] = {ok ? vr[k].x : 0u, ok ? vr[k].y : 0u, ok ? vr[k].z : 0u,
+                               ok ? vr[k].w : 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v0 = lo_f(w[e], DT()), v1 = hi_f(w[e], DT());
+#pragma unroll
+          for (int g = 0; g < GQ; ++g) {
+            o[g][2 * e] += pb[k][g] * v0;
+            o[g][2 * e + 1] += pb[k][g] * v1;
+          }
+        }
+      }
+      if (nt) load_v(nt);   // V consumed: fetch the next unit's V
+    }
   }
+  if (cur_j >= 0) end_head(cur_j);
 }
 
 // Split that owns unit u when U units are cut into S ranges starting at
@@ -206,9 +330,15 @@ __device__ __forceinline__ int split_of(int64_t u, int64_t U, int64_t S) {
   return (int)(((u + 1) * S - 1) / U);
 }
 
+// One wave per (request, query head).  The splits that touched the head form
+// a contiguous range [s_lo, s_hi]; M = max lse and the weights 2^(lse - M)
+// are formed lane-parallel, then 8 splits are merged per step: lane l takes
+// split l / 8 of the step and channels (l % 8) * D/8 .. +D/8, and the 8 split
+// lanes of each channel chunk are summed with DPP / lane swaps at the end.
 template <int D>
 __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a) {
-  constexpr int PER = D / 64;   // channels per lane
+  constexpr int CH = D / 8;          // channels per lane
+  constexpr int V4 = CH / 4;         // float4 loads per split row
   __shared__ GroupUnits gu;
   const CacheView& c = a.c;
   const int lane = threadIdx.x;
@@ -217,42 +347,62 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a) {
   const int h = g / c.Gq;
   const int hs = c.head_slot[h];
   float* dst = a.out + ((int64_t)r * c.Hq + g) * D;
-  if (hs < 0 || hs >= c.Hkv) {
-    for (int e = lane; e < D; e += 64) dst[e] = 0.f;
-    return;
-  }
-  const int gi = hs / c.Hp, j = hs % c.Hp;
+  const int gi = (hs >= 0 && hs < c.Hkv) ? hs / c.Hp : 0, j = (hs >= 0 && hs < c.Hkv) ? hs % c.Hp : 0;
   group_units(a, r, gi, &gu);
   const int64_t U = gu.total;
-  const int Si = a.S_prefix[gi + 1] - a.S_prefix[gi];
-  float acc[PER];
+  const int64_t Si = a.S_prefix[gi + 1] - a.S_prefix[gi];
+  const bool live = hs >= 0 && hs < c.Hkv && gu.head[j] == h && gu.count[j] > 0;
+  const int s_lo = live ? split_of(gu.start[j], U, Si) : 0;
+  const int s_hi = live ? split_of(gu.start[j] + gu.count[j] - 1, U, Si) : -1;
+  const int64_t row = ((int64_t)r * c.Hq + g) * a.Smax;
+  // A split whose unit range is empty wrote nothing (possible when U < S_i).
+  auto lse_of = [&](int s) {
+    const bool ok = s <= s_hi && (s * U) / Si < ((s + 1) * U) / Si;
+    return ok ? a.lse_part[row + s] : -__builtin_inff();
+  };
+  float M = -__builtin_inff();
+  for (int s = s_lo + lane; s <= s_hi; s += 64) M = fmaxf(M, lse_of(s));
+  M = group_max<64>(M);
+  float acc[CH];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
-  if (gu.count[j] > 0) {
-    const int s_lo = split_of(gu.start[j], U, Si);
-    const int s_hi = split_of(gu.start[j] + gu.count[j] - 1, U, Si);
-    const int64_t row = ((int64_t)r * c.Hq + g) * a.Smax;
-    // A split whose unit range is empty wrote nothing (possible when U < S_i).
-    auto nonempty = [&](int64_t s) { return (s * U) / Si < ((s + 1) * U) / Si; };
-    float M = -__builtin_inff();
-    for (int s = s_lo; s <= s_hi; ++s)
-      if (nonempty(s)) M = fmaxf(M, a.lse_part[row + s]);
-    if (M > -__builtin_inff()) {
-      float den = 0.f;
-      for (int s = s_lo; s <= s_hi; ++s) {
-        if (!nonempty(s)) continue;
-        const float w = exp2f(a.lse_part[row + s] - M);
+  for (int e = 0; e < CH; ++e) acc[e] = 0.f;
+  float den = 0.f;
+  const int sl = lane / 8, dc = lane % 8;
+  if (M > -__builtin_inff()) {
+    for (int s0 = s_lo; s0 <= s_hi; s0 += 8) {
+      const int s = s0 + sl;
+      const float w = s <= s_hi ? __builtin_amdgcn_exp2f(lse_of(s) - M) : 0.f;
+      if (w > 0.f) {
         den += w;
-        const float* src = a.o_part + (row + s) * D;
+        const float4* src = reinterpret_cast<const float4*>(a.o_part + (row + s) * D + dc * CH);
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] += w * src[lane * PER + e];
+        for (int v = 0; v < V4; ++v) {
+          const float4 x = src[v];
+          acc[4 * v] += w * x.x;
+          acc[4 * v + 1] += w * x.y;
+          acc[4 * v + 2] += w * x.z;
+          acc[4 * v + 3] += w * x.w;
+        }
       }
-#pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] /= den;
     }
   }
+  // sum over the 8 split lanes (lane bits 3..5) of each channel chunk
+  den = group_sum<64>(den) * (1.f / 8.f);   // every split lane counted each weight once; dc copies x8
 #pragma unroll
-  for (int e = 0; e < PER; ++e) dst[lane * PER + e] = acc[e];
+  for (int e = 0; e < CH; ++e) {
+    float v = acc[e];
+    v += dpp<0x128>(v);   // row_ror:8 -> lane ^ 8 within a row of 16
+    v = across_sum<16>(v);
+    acc[e] = v;
+  }
+  if (sl == 0) {
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    float4* o4 = reinterpret_cast<float4*>(dst + dc * CH);
+#pragma unroll
+    for (int v = 0; v < V4; ++v)
+      o4[v] = make_float4(acc[4 * v] * inv, acc[4 * v + 1] * inv, acc[4 * v + 2] * inv,
+                          acc[4 * v + 3] * inv);
+  }
 }
 
 template <int D, int GQ, typename DT>

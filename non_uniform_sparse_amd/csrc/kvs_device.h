@@ -51,33 +51,93 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi, BF16 t) {
   return narrow(lo, t) | (narrow(hi, t) << 16);
 }
 
-// Butterfly reductions over aligned lane groups of width W (a power of two,
-// W <= 64).  Every lane of a group ends with the same, bitwise identical,
-// result: at each level both partners add the same two partial values.
+// Cross-lane moves without LDS.  DPP row patterns (a row is 16 lanes):
+// quad_perm [1,0,3,2] = lane ^ 1, quad_perm [2,3,0,1] = lane ^ 2,
+// row_half_mirror = 7 - (lane & 7), row_mirror = 15 - (lane & 15).
+// v_permlane16_swap(x, x) returns {rows 0,0,2,2 ; rows 1,1,3,3} and
+// v_permlane32_swap(x, x) returns {lanes 0-31 twice ; lanes 32-63 twice},
+// so the sum of the pair is x + x[lane ^ 16] (resp. x[lane ^ 32]).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ void swap16(float v, float* a, float* b) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  *a = __uint_as_float(r[0]);
+  *b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap32(float v, float* a, float* b) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  *a = __uint_as_float(r[0]);
+  *b = __uint_as_float(r[1]);
+}
+
+// Sum / max over aligned groups of W lanes (W a power of two, 2..64).  Each
+// level combines a lane with its partner in the other half of the group;
+// once the values are uniform inside each half, mirror partners are as
+// good as xor partners.  Every lane of a group ends with the same bitwise
+// result: both partners combine the same two values.
 template <int W>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int m = 1; m < W; m <<= 1) v += __shfl_xor(v, m, 64);
+  static_assert(W >= 2 && W <= 64 && (W & (W - 1)) == 0, "group width");
+  v += dpp<0xB1>(v);
+  if (W >= 4) v += dpp<0x4E>(v);
+  if (W >= 8) v += dpp<0x141>(v);
+  if (W >= 16) v += dpp<0x140>(v);
+  if (W >= 32) {
+    float a, b;
+    swap16(v, &a, &b);
+    v = a + b;
+  }
+  if (W >= 64) {
+    float a, b;
+    swap32(v, &a, &b);
+    v = a + b;
+  }
   return v;
 }
 template <int W>
 __device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-  for (int m = 1; m < W; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  static_assert(W >= 2 && W <= 64 && (W & (W - 1)) == 0, "group width");
+  v = fmaxf(v, dpp<0xB1>(v));
+  if (W >= 4) v = fmaxf(v, dpp<0x4E>(v));
+  if (W >= 8) v = fmaxf(v, dpp<0x141>(v));
+  if (W >= 16) v = fmaxf(v, dpp<0x140>(v));
+  if (W >= 32) {
+    float a, b;
+    swap16(v, &a, &b);
+    v = fmaxf(a, b);
+  }
+  if (W >= 64) {
+    float a, b;
+    swap32(v, &a, &b);
+    v = fmaxf(a, b);
+  }
   return v;
 }
-// Reduce across lanes that differ in the bits >= FROM (lane ^ FROM, lane ^ 2*FROM, ...).
+// Sum / max across lanes that differ only in lane bits >= FROM (FROM = 16
+// or 32): combines the 64/FROM row groups holding the same columns.
 template <int FROM>
 __device__ __forceinline__ float across_sum(float v) {
-#pragma unroll
-  for (int m = FROM; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
-  return v;
+  static_assert(FROM == 16 || FROM == 32, "across width");
+  float a, b;
+  if (FROM == 16) {
+    swap16(v, &a, &b);
+    v = a + b;
+  }
+  swap32(v, &a, &b);
+  return a + b;
 }
 template <int FROM>
 __device__ __forceinline__ float across_max(float v) {
-#pragma unroll
-  for (int m = FROM; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-  return v;
+  static_assert(FROM == 16 || FROM == 32, "across width");
+  float a, b;
+  if (FROM == 16) {
+    swap16(v, &a, &b);
+    v = fmaxf(a, b);
+  }
+  swap32(v, &a, &b);
+  return fmaxf(a, b);
 }
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }

@@ -6,7 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/kvs.h"
+#include "kvs.h"
 
 namespace kvs {
 

@@ -1,18 +1,19 @@
 // Per-KV-head top-K page selection (FlexiCache summary, Core method: each
-// head attends only its K best pages).  One 256-thread workgroup per
-// (request, head).  Scores become order-preserving 32-bit keys held in LDS;
-// a most-significant-digit radix select (4 passes of 8 bits, LDS histogram)
-// finds the K-th largest key tau; pages with key > tau are kept, and among
-// pages with key == tau the lowest page indices fill the remaining places.
-// Two block-wide exclusive scans in page order (equal keys, then kept pages)
-// rank the ties and place the kept pages in ascending page order.  Integer
-// work only, so the result is deterministic.
+// head attends only its K best pages).  One wave per (request, head).
+// Scores become order-preserving 32-bit keys held in LDS; a most-significant-
+// digit radix select (4 passes of 8 bits) finds the K-th largest key tau:
+// a pass whose candidate keys (those matching the digits chosen so far) all
+// share one digit takes it directly; otherwise it builds a 256-bin LDS
+// histogram of the candidates, every lane owns 4 bins, a suffix scan over lanes gives the
+// count above each lane's bins and the one lane whose bins straddle the K-th
+// key publishes the digit.  Pages with key > tau are kept, and among pages
+// with key == tau the lowest page indices fill the remaining places; ballots
+// over 64-page windows rank the ties and place the kept pages in ascending
+// page order.  Integer work only, so the result is deterministic.
 #include "kvs_device.h"
 
 namespace kvs {
 namespace {
-
-constexpr int kThreads = 256;
 
 // Larger float -> larger key; -0 and +0 map to the same key.
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -21,106 +22,114 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive scan of one int per thread over the workgroup; returns the
-// thread's prefix and writes the total to *total.
-__device__ int block_exclusive_scan(int v, int* lds, int* total) {
-  const int tid = threadIdx.x;
-  lds[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    const int add = tid >= off ? lds[tid - off] : 0;
-    __syncthreads();
-    lds[tid] += add;
-    __syncthreads();
-  }
-  const int incl = lds[tid];
-  *total = lds[kThreads - 1];
-  __syncthreads();
-  return incl - v;
+// Number of set bits of m in lanes below this one.
+__device__ __forceinline__ int rank_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-__global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ scores,
-                                                        const int32_t* __restrict__ seq_len, int P,
-                                                        int Hkv, int max_pages, int K,
-                                                        int32_t* __restrict__ sel,
-                                                        int32_t* __restrict__ sel_count) {
-  __shared__ uint32_t keys[kMaxTopkPages];
+__global__ __launch_bounds__(64) void topk_kernel(const float* __restrict__ scores,
+                                                  const int32_t* __restrict__ seq_len, int P,
+                                                  int max_pages, int K, int32_t* __restrict__ sel,
+                                                  int32_t* __restrict__ sel_count) {
+  extern __shared__ uint32_t keys[];   // [max_pages]
   __shared__ int hist[256];
-  __shared__ int scan[kThreads];
-  __shared__ uint32_t s_prefix;
-  __shared__ int s_need;
-
   const int rh = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int lane = threadIdx.x;
   const int n = clampi(seq_len[rh], 0, P * max_pages);
   const int npg = (n + P - 1) / P;
   const int keep = min(K, npg);
   const float* row = scores + (int64_t)rh * max_pages;
   int32_t* out = sel + (int64_t)rh * K;
 
-  for (int p = tid; p < npg; p += kThreads) keys[p] = order_key(row[p]);
-  if (tid == 0) {
-    s_prefix = 0;
-    s_need = keep;
-  }
-  __syncthreads();
+  for (int p = lane; p < npg; p += 64) keys[p] = order_key(row[p]);
 
-  // Radix select of the keep-th largest key.
-  uint32_t mask = 0;
+  uint32_t prefix = 0, mask = 0;
+  int need = keep;   // keys equal to the final prefix still to take
   for (int shift = 24; shift >= 0 && keep > 0; shift -= 8) {
-    hist[tid] = 0;  // kThreads == 256 bins
+    // Scores of one head often share their top bits: if every candidate key
+    // has the same digit, it is the digit, with no histogram (and no
+    // 64-way atomic contention on one bin).
+    int dmin = 256, dmax = -1;
+    for (int p = lane; p < npg; p += 64) {
+      const uint32_t k = keys[p];
+      if ((k & mask) == prefix) {
+        const int dg = (int)((k >> shift) & 255u);
+        dmin = min(dmin, dg);
+        dmax = max(dmax, dg);
+      }
+    }
+    dmin = (int)group_max<64>(-(float)dmin) * -1;
+    dmax = (int)group_max<64>((float)dmax);
+    if (dmin == dmax) {
+      prefix |= (uint32_t)dmin << shift;
+      mask |= 255u << shift;
+      continue;
+    }
+    for (int b = lane; b < 256; b += 64) hist[b] = 0;
     __syncthreads();
-    const uint32_t prefix = s_prefix;
-    for (int p = tid; p < npg; p += kThreads) {
+    for (int p = lane; p < npg; p += 64) {
       const uint32_t k = keys[p];
       if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1);
     }
     __syncthreads();
-    if (tid == 0) {
-      int need = s_need, digit = 255;
-      for (; digit > 0; --digit) {
-        if (hist[digit] >= need) break;
-        need -= hist[digit];
-      }
-      s_prefix = prefix | ((uint32_t)digit << shift);
-      s_need = need;
+    int hb[4], mine = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hb[i] = hist[4 * lane + i];
+      mine += hb[i];
     }
+    // inclusive suffix sum over lanes (lane 63 holds the largest digits)
+    int incl = mine;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_down(incl, off, 64);
+      if (lane + off < 64) incl += t;
+    }
+    int acc = incl - mine;   // keys in bins above this lane's
+    int found = -1, left = 0;
+#pragma unroll
+    for (int i = 3; i >= 0; --i) {
+      if (found < 0 && acc < need && need <= acc + hb[i]) {
+        found = 4 * lane + i;
+        left = need - acc;
+      }
+      acc += hb[i];
+    }
+    const uint64_t who = __ballot(found >= 0);
+    const int src = __builtin_ctzll(who);
+    prefix |= (uint32_t)__shfl(found, src, 64) << shift;
+    need = __shfl(left, src, 64);
     mask |= 255u << shift;
     __syncthreads();
   }
-  const uint32_t tau = s_prefix;
-  const int ties = s_need;   // pages equal to tau still to take
+  const uint32_t tau = prefix;
+  const int ties = need;
 
-  // Contiguous page range of this thread, in page order.
-  const int per = (npg + kThreads - 1) / kThreads;
-  const int p0 = min(npg, tid * per), p1 = min(npg, p0 + per);
-  int eq = 0;
-  for (int p = p0; p < p1; ++p) eq += keys[p] == tau;
-  int total;
-  int eq_before = block_exclusive_scan(eq, scan, &total);
-  int kept = 0;
-  for (int p = p0; p < p1; ++p) {
-    const uint32_t k = keys[p];
-    if (k > tau || (k == tau && eq_before++ < ties)) ++kept;
+  int eq_before = 0, pos_before = 0;
+  for (int base = 0; base < npg; base += 64) {
+    const int p = base + lane;
+    const uint32_t k = p < npg ? keys[p] : 0u;
+    const bool eq = p < npg && k == tau;
+    const uint64_t eqm = __ballot(eq);
+    const bool take = keep > 0 && p < npg && (k > tau || (eq && eq_before + rank_below(eqm) < ties));
+    const uint64_t tm = __ballot(take);
+    const int pos = pos_before + rank_below(tm);
+    if (take && pos < keep) out[pos] = p;
+    eq_before += __popcll(eqm);
+    pos_before += __popcll(tm);
   }
-  int pos = block_exclusive_scan(kept, scan, &total);
-  eq_before -= eq;   // rewind to this range's first tie rank
-  if (keep > 0) {
-    for (int p = p0; p < p1; ++p) {
-      const uint32_t k = keys[p];
-      if (k > tau || (k == tau && eq_before++ < ties)) out[pos++] = p;
-    }
-  }
-  for (int k = keep + tid; k < K; k += kThreads) out[k] = -1;
-  if (tid == 0) sel_count[rh] = keep;
+  for (int k = keep + lane; k < K; k += 64) out[k] = -1;
+  if (lane == 0) sel_count[rh] = keep;
 }
 
 }  // namespace
 
 hipError_t launch_topk(const float* scores, const int32_t* seq_len, int P, int b, int Hkv,
                        int max_pages, int K, int32_t* sel, int32_t* sel_count, hipStream_t s) {
-  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)(b * Hkv)), dim3(kThreads), 0, s, scores, seq_len,
-                     P, Hkv, max_pages, K, sel, sel_count);
+  const size_t lds = (size_t)max_pages * sizeof(uint32_t);
+  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)(b * Hkv)), dim3(64), lds, s, scores, seq_len, P,
+                     max_pages, K, sel, sel_count);
   return hipGetLastError();
 }
 
