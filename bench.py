@@ -114,6 +114,52 @@ def cpu_baseline(wl, step, budget_s: float = 12.0) -> dict:
                       f"{done_bytes / 1e6:.1f} MB of KV in {spent:.1f} s"}
 
 
+def skew_report(configs, launches: int = 20) -> dict:
+    """Per-workgroup duration skew of the split-K decode kernel, max / mean
+    over the workgroups of one launch, median over launches, per layer; with
+    the planned split map and with a uniform one of the same total (equal
+    budgets).  Uses the stamp-instrumented library build."""
+    from non_uniform_sparse_amd import build as B
+    kvs.use_library(B.LIB_STAMPS)
+    out = {}
+    for name in configs:
+        wl = make_workload(name)
+        c = wl.cfg
+        step = DecodeStep(wl, device="cuda:0")
+        qs = step.queries()
+        if c.topk:
+            for l in range(c.L):
+                step.select(l, qs[l])
+        res = {}
+        for label in ("planned", "uniform"):
+            per_layer = []
+            for l in range(c.L):
+                T = int(step.S[l].sum())
+                row = step.S[l] if label == "planned" else kvs.kvs_plan_split(
+                    np.ones((1, c.Hkv)), step.head_slot[l:l + 1], c.Hp, 0.0, T)[0]
+                need = kvs.kvs_decode_workspace_bytes(c.b, c.Hq, c.Hkv, c.d, row)
+                if need > step.workspace.numel():
+                    step.workspace = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+                off = kvs.kvs_decode_stamps_offset(c.b, c.Hq, c.Hkv, c.d, row)
+                nwg = c.b * int(np.sum(row))
+                skews = []
+                for _ in range(launches):
+                    step.attend(l, qs[l], S_row=row)
+                    torch.cuda.synchronize()
+                    st = step.workspace[off:off + nwg * 16].view(torch.int64).view(nwg, 2).cpu()
+                    dur = (st[:, 1] - st[:, 0]).double()
+                    skews.append(float(dur.max() / dur.mean()))
+                per_layer.append(statistics.median(skews))
+            res[label] = {"median_over_layers": round(statistics.median(per_layer), 3),
+                          "max_over_layers": round(max(per_layer), 3),
+                          "per_layer": [round(x, 3) for x in per_layer]}
+        res["splits_per_request"] = step.T
+        out[name] = res
+        del step
+        torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +168,12 @@ def main() -> int:
     ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--skew", nargs="*", default=None, metavar="CONFIG",
+                    help="measure per-workgroup duration skew (planned vs uniform split "
+                         "map) with the instrumented build, print it and exit")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only a plain 1 GiB device copy (known bytes) to scale "
+                         "hardware byte counters, then exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the decode path here runs on a single MI355X "
@@ -130,6 +182,25 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.skew is not None:
+        print(json.dumps({"skew": skew_report(args.skew or ["llama8b_ragged", "longctx_skew"])}))
+        return 0
+    if args.copy_probe:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        times = []
+        for _ in range(5):
+            a.record()
+            dst.copy_(src)
+            b.record()
+            b.synchronize()
+            times.append(a.elapsed_time(b))
+        print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n,
+                          "ms": round(min(times), 4),
+                          "GBps_read_plus_write": round(2 * n / (min(times) * 1e-3) / 1e9, 1)}))
+        return 0
 
     t0 = time.time()
     wl = make_workload(args.config)
@@ -141,8 +212,6 @@ def main() -> int:
         f"S[0]={step.S[0].tolist()}")
 
     stream = torch.cuda.Stream()
-    # Small working sets are flushed from L2 / MALL before each step.
-    flush = None
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
             step.run(qs, stream)
@@ -150,20 +219,17 @@ def main() -> int:
     ab = [algorithmic_bytes(step, l) for l in range(c.L)]
     kv_bytes = sum(a["kv"] for a in ab)
     path_bytes = sum(a["kv"] + a["meta"] + a["small"] for a in ab)
-    if path_bytes < 8e9:
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-
+    # Working sets that could sit in L2 / MALL (256 MB) are flushed before each step.
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if path_bytes < 8e9 else None
     ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    # Pass 1 (eager, per-kernel HIP events on the launch stream): kernel
+    # durations for the roofline figures.
     kern = {"score": [], "topk": [], "decode_attn": []}
-    step_ms = []
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
     for _ in range(args.steps):
         if flush is not None:
             with torch.cuda.stream(stream):
                 flush.zero_()
-        s0, s1 = ev(), ev()
-        s0.record(stream)
         marks = []
         for l in range(c.L):
             q = qs[l]
@@ -182,11 +248,29 @@ def main() -> int:
             step.attend(l, q, stream)
             e1.record(stream)
             marks.append(("decode_attn", e0, e1))
-        s1.record(stream)
         stream.synchronize()
-        step_ms.append(s0.elapsed_time(s1))
         for k, a, b_ in marks:
             kern[k].append(a.elapsed_time(b_))
+
+    # Pass 2 (headline): the whole step captured once as a HIP graph and
+    # replayed; K steps timed between two synchronisations.
+    graph = step.capture(qs)
+    cur = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    step_ms = []
+    wall0 = time.perf_counter()
+    for _ in range(args.steps):
+        if flush is not None:
+            flush.zero_()
+        s0, s1 = ev(), ev()
+        s0.record(cur)
+        graph.replay()
+        s1.record(cur)
+        if flush is not None:
+            s1.synchronize()
+            step_ms.append(s0.elapsed_time(s1))
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - wall0) * 1e3
 
@@ -217,6 +301,7 @@ def main() -> int:
             "topk_pages": c.topk, "splits_per_request": step.T,
             "kv_bytes_per_step": kv_bytes, "path_bytes_per_step": path_bytes,
             "cache_flush_between_steps": flush is not None,
+            "step_launch": "hip_graph",
         },
         "kernels_ms_avg": {k: round(statistics.mean(v), 5) for k, v in kern.items() if v},
         "roofline": {

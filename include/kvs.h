@@ -172,9 +172,10 @@ int kvs_decode_attn(const kvs_paged_kv* cache, const void* q, const int32_t* sel
                     void* workspace, size_t ws_bytes, float* out, void* stream);
 
 /* Bytes of workspace kvs_decode_attn needs for this shape and split row
- * (per-split partial outputs and log-sum-exps).  0 on bad arguments. */
-size_t kvs_decode_workspace_bytes(int32_t b, int32_t Hq, int32_t d, const int32_t* S_row,
-                                  int32_t G);
+ * (per-split partial outputs and log-sum-exps, and each head's first and
+ * last split).  0 on bad arguments. */
+size_t kvs_decode_workspace_bytes(int32_t b, int32_t Hq, int32_t Hkv, int32_t d,
+                                  const int32_t* S_row, int32_t G);
 
 /* Concurrent decode workgroups on `device` for this kernel variant [T 3.3:
  * the split map is sized to what the chip runs at once]:

@@ -13,6 +13,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvs.so")
+# Instrumented variant: decode workgroups record start/end stamps (skew runs only).
+LIB_STAMPS = os.path.join(PKG, "libkvs_stamps.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -26,10 +28,10 @@ def sources(csrc: str = CSRC):
     return sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str, csrc: str = CSRC, build_dir: str = BUILD) -> str:
+def _compile(src: str, csrc: str = CSRC, build_dir: str = BUILD, defines=()) -> str:
     obj = os.path.join(build_dir, src + ".o")
     path = os.path.join(csrc, src)
-    flags = [f"-I{os.path.join(ROOT, 'include')}", f"-I{csrc}", *COMMON]
+    flags = [f"-I{os.path.join(ROOT, 'include')}", f"-I{csrc}", *COMMON, *defines]
     if src.endswith(".hip"):
         cmd = [HIPCC, "-x", "hip", *DEVICE, *flags, "-c", path, "-o", obj]
     else:  # host-only C++
@@ -41,12 +43,12 @@ def _compile(src: str, csrc: str = CSRC, build_dir: str = BUILD) -> str:
 
 
 def build(verbose: bool = False, csrc: str = CSRC, lib: str = LIB,
-          build_dir: str = BUILD) -> str:
+          build_dir: str = BUILD, defines=()) -> str:
     """Compile every source under ``csrc`` and link ``lib``."""
     os.makedirs(build_dir, exist_ok=True)
     srcs = sources(csrc)
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda f: _compile(f, csrc, build_dir), srcs))
+        objs = list(ex.map(lambda f: _compile(f, csrc, build_dir, defines), srcs))
     tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -58,6 +60,12 @@ def build(verbose: bool = False, csrc: str = CSRC, lib: str = LIB,
     return lib
 
 
+def build_all(verbose: bool = False) -> None:
+    """The library and its workgroup-stamp instrumented variant."""
+    build(verbose)
+    build(verbose, lib=LIB_STAMPS, build_dir=BUILD + "_stamps", defines=("-DKVS_WG_STAMPS",))
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    build_all(verbose=True)
     sys.exit(0)

@@ -64,11 +64,18 @@ int check_cache(const kvs_paged_kv* p, bool need_minmax, const char* fn, CacheVi
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Partial outputs then log-sum-exps: [b][Hq][Smax][d] f32, [b][Hq][Smax] f32.
-size_t workspace_bytes(int b, int Hq, int d, int Smax) {
+// Partial outputs, log-sum-exps, then each head's split range:
+// [b][Hq][Smax][d] f32, [b][Hq][Smax] f32, [b][Hkv] i32 (first), [b][Hkv] i32 (last).
+size_t workspace_bytes(int b, int Hq, int Hkv, int d, int Smax) {
   const size_t rows = (size_t)b * Hq * Smax;
-  return round256(rows * d * sizeof(float)) + round256(rows * sizeof(float));
+  return round256(rows * d * sizeof(float)) + round256(rows * sizeof(float)) +
+         2 * round256((size_t)b * Hkv * sizeof(int32_t));
 }
+
+#ifdef KVS_WG_STAMPS
+// Instrumented build: per-workgroup start/end stamps follow the workspace.
+size_t stamp_bytes(int b, int splits_total) { return round256((size_t)b * splits_total * 16); }
+#endif
 
 }  // namespace
 
@@ -151,13 +158,17 @@ int check_splits(const int32_t* S_row, int G, int b, DecodeArgs* a, int* smax, c
 }
 }  // namespace
 
-extern "C" size_t kvs_decode_workspace_bytes(int32_t b, int32_t Hq, int32_t d,
+extern "C" size_t kvs_decode_workspace_bytes(int32_t b, int32_t Hq, int32_t Hkv, int32_t d,
                                              const int32_t* S_row, int32_t G) {
-  if (b < 1 || Hq < 1 || d < 1 || G < 1 || G > kMaxGroups || !S_row) return 0;
+  if (b < 1 || Hq < 1 || Hkv < 1 || d < 1 || G < 1 || G > kMaxGroups || !S_row) return 0;
   DecodeArgs a;
   int smax = 0;
   if (check_splits(S_row, G, b, &a, &smax, "kvs_decode_workspace_bytes")) return 0;
-  return workspace_bytes(b, Hq, d, smax);
+#ifdef KVS_WG_STAMPS
+  return workspace_bytes(b, Hq, Hkv, d, smax) + stamp_bytes(b, a.splits_total);
+#else
+  return workspace_bytes(b, Hq, Hkv, d, smax);
+#endif
 }
 
 extern "C" int kvs_decode_attn(const kvs_paged_kv* cache, const void* q, const int32_t* sel,
@@ -177,7 +188,11 @@ extern "C" int kvs_decode_attn(const kvs_paged_kv* cache, const void* q, const i
   if (!(scale > 0.f) || !(scale < 1e30f)) return set_error(KVS_EINVAL, "%s: bad scale", fn);
   int smax = 0;
   if (int rc = check_splits(S_row, a.c.G, a.c.b, &a, &smax, fn)) return rc;
-  const size_t need = workspace_bytes(a.c.b, a.c.Hq, a.c.d, smax);
+  size_t need = workspace_bytes(a.c.b, a.c.Hq, a.c.Hkv, a.c.d, smax);
+#ifdef KVS_WG_STAMPS
+  const size_t stamps_at = need;
+  need += stamp_bytes(a.c.b, a.splits_total);
+#endif
   if (ws_bytes < need)
     return set_error(KVS_ENOSPC, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
   a.q = q;
@@ -186,9 +201,18 @@ extern "C" int kvs_decode_attn(const kvs_paged_kv* cache, const void* q, const i
   a.K = sel ? K : 0;
   a.scale_log2 = scale * kLog2e;
   a.Smax = smax;
-  a.o_part = static_cast<float*>(workspace);
-  a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                        round256((size_t)a.c.b * a.c.Hq * smax * a.c.d * 4));
+  char* ws = static_cast<char*>(workspace);
+  const size_t rows = (size_t)a.c.b * a.c.Hq * smax;
+  a.o_part = reinterpret_cast<float*>(ws);
+  ws += round256(rows * a.c.d * sizeof(float));
+  a.lse_part = reinterpret_cast<float*>(ws);
+  ws += round256(rows * sizeof(float));
+  a.split_lo = reinterpret_cast<int32_t*>(ws);
+  ws += round256((size_t)a.c.b * a.c.Hkv * sizeof(int32_t));
+  a.split_hi = reinterpret_cast<int32_t*>(ws);
+#ifdef KVS_WG_STAMPS
+  a.stamps = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + stamps_at);
+#endif
   a.out = out;
   hipStream_t s = (hipStream_t)stream;
   if (hipError_t e = launch_decode(a, s)) return hip_error(e, "kvs_decode_attn (split kernel)");
@@ -213,3 +237,16 @@ extern "C" int kvs_decode_concurrency(int32_t device, int32_t d, int32_t gqa, in
   *W = cus * blocks;
   return KVS_OK;
 }
+
+#ifdef KVS_WG_STAMPS
+// Instrumented build only: byte offset of the [b * sum(S_row)][2] uint64
+// start/end stamps (s_memrealtime, 100 MHz) inside the decode workspace.
+extern "C" size_t kvs_decode_stamps_offset(int32_t b, int32_t Hq, int32_t Hkv, int32_t d,
+                                           const int32_t* S_row, int32_t G) {
+  if (b < 1 || Hq < 1 || Hkv < 1 || d < 1 || G < 1 || G > kMaxGroups || !S_row) return 0;
+  DecodeArgs a;
+  int smax = 0;
+  if (check_splits(S_row, G, b, &a, &smax, "kvs_decode_stamps_offset")) return 0;
+  return workspace_bytes(b, Hq, Hkv, d, smax);
+}
+#endif

@@ -9,9 +9,10 @@
 // units and S_i splits, split s owns units [floor(s U/S_i), floor((s+1) U/S_i)).
 // One 64-lane workgroup (one wave) per (r, i, s) walks its units in order,
 // keeping an online softmax per query head of the KV head it is in, and
-// emits a partial (o, lse) for every head it touched.  The combine kernel
-// finds, for each query head, the contiguous splits that touched its KV head
-// and merges them.
+// emits a partial (o, lse) for every head it touched, noting for each head
+// whether it is that head's first or last split.  The combine kernel merges,
+// for each query head, the contiguous range of splits that touched its KV
+// head.
 //
 // Lane layout for one page of one head (P = 16 rows of d 16-bit elements):
 // lane l takes channels 8*(l % COLS) .. +8 of rows rg + RPL*k, rg = l / COLS,
@@ -125,7 +126,10 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   using Geo = Geometry<D>;
   constexpr int COLS = Geo::COLS, RPL = Geo::RPL, TL = Geo::TL, A = Geo::A, KB = Geo::KB;
   static_assert(GQ <= 16, "query group must fit the 16 MFMA columns");
+  constexpr int KROW = D + 8;                 // LDS row stride (halves): 16 B pad
   __shared__ GroupUnits gu;
+  __shared__ uint4 ktile_raw[P * KROW / 8];    // one page's K tile, row-major
+  uint16_t* ktile = reinterpret_cast<uint16_t*>(ktile_raw);
   const CacheView& c = a.c;
   const int lane = threadIdx.x;
   const int r = blockIdx.x / a.splits_total;
@@ -134,20 +138,55 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   while (rem >= a.S_prefix[gi + 1]) ++gi;
   const int Si = a.S_prefix[gi + 1] - a.S_prefix[gi];
   const int s = rem - a.S_prefix[gi];
+#ifdef KVS_WG_STAMPS
+  const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
+  struct Stamp {
+    uint64_t* p;
+    uint64_t t0;
+    __device__ ~Stamp() {
+      if (threadIdx.x == 0) {
+        p[0] = t0;
+        p[1] = __builtin_amdgcn_s_memrealtime();
+      }
+    }
+  } stamp{a.stamps + 2 * (int64_t)blockIdx.x, t_start};
+#endif
 
   group_units(a, r, gi, &gu);
   const int64_t U = gu.total;
   const int u0 = (int)((int64_t)s * U / Si), u1 = (int)((int64_t)(s + 1) * U / Si);
-  if (u0 >= u1) return;
+  if (u0 >= u1) {
+    // An empty split (U < S_i) that lies strictly inside a head's range of
+    // splits marks itself as holding nothing, so the combine can walk the
+    // range [first, last] of that head without knowing U.
+    if (lane < c.Hp) {
+      const int st = gu.start[lane], en = st + gu.count[lane], h = gu.head[lane];
+      if (h >= 0 && st < u0 && u0 < en) {
+        for (int g = 0; g < GQ; ++g)
+          a.lse_part[((int64_t)r * c.Hq + h * GQ + g) * a.Smax + s] = -__builtin_inff();
+      }
+    }
+    return;
+  }
+  // For each head this split touches: is it the head's first / last split?
+  if (lane < c.Hp) {
+    const int st = gu.start[lane], en = st + gu.count[lane], h = gu.head[lane];
+    if (h >= 0 && gu.count[lane] > 0 && u0 < en && u1 > st) {
+      const int64_t hidx = (int64_t)r * c.Hkv + h;
+      if (u0 <= st) a.split_lo[hidx] = s;
+      if (u1 >= en) a.split_hi[hidx] = s;
+    }
+  }
 
-  // V-side role
+  // V-side role (also how K is fetched: RPL whole rows per load instruction)
   const int rg = lane / COLS, vcol = lane % COLS;
   const int v_off = rg * D + 8 * vcol;
   // MFMA roles: operand row m = lane % 16 (a token), k sub-block kq = lane / 16
   const int m = lane % 16, kq = lane / 16;
   const int ka = m / 4, ki = m % 4;
-  const int k_tok = (ka / A) + RPL * (4 * (ka % A) + ki);   // token loaded as MFMA row m
-  const int k_off = k_tok * D + 8 * kq;
+  const int k_tok = (ka / A) + RPL * (4 * (ka % A) + ki);   // token fed as MFMA row m
+  const int k_lds = k_tok * KROW + 8 * kq;                  // its operand slice in LDS
+  const int w_lds = rg * KROW + 8 * vcol;                   // where this lane stores K rows
   // result role: column (query head) rcol, row group ra holding 4 tokens
   const int rcol = lane % 16, ra = lane / 16;
   const int r_tok0 = (ra / A) + RPL * 4 * (ra % A);          // token of element i: r_tok0 + RPL*i
@@ -164,9 +203,14 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   auto begin_head = [&](int j) {
     const int h = gu.head[j];
     const bool has = rcol < GQ;
+    // unconditional loads (columns >= GQ read row 0 and are zeroed), so no
+    // branch hides them from the wait-count bookkeeping of the loop
     const uint16_t* qrow = qb + ((int64_t)r * c.Hq + h * GQ + (has ? rcol : 0)) * D + 8 * kq;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) qop[kb] = has ? ld16(qrow + 32 * kb) : make_uint4(0, 0, 0, 0);
+    for (int kb = 0; kb < KB; ++kb) {
+      const uint4 v = ld16(qrow + 32 * kb);
+      qop[kb] = has ? v : make_uint4(0, 0, 0, 0);
+    }
     m_col = -__builtin_inff();
     l_col = 0.f;
 #pragma unroll
@@ -200,7 +244,10 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     }
   };
 
-  uint4 kr[KB], vr[TL];
+  // Pages in flight per wave: two for d = 128 (8 KB pages), one for d = 256
+  // (16 KB pages), at the same occupancy.
+  constexpr int DEPTH = D == 128 ? 2 : 1;
+  uint4 kc[DEPTH][TL], vr[DEPTH][TL];   // K and V rows of upcoming units, coalesced layout
   for (int base = u0; base < u1; base += 64) {
     const int nb = min(64, u1 - base);
     // Lane t resolves unit base + t: its slot, physical page and valid rows.
@@ -223,48 +270,63 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
       }
       my_j = j;
     }
+    // Tile of unit t; a missing page reads page 0 instead (always valid
+    // memory; such units are skipped), so every load is unconditional.
     auto tile = [&](int t) {
       const int phys = __builtin_amdgcn_readlane(my_phys, t);
       const int j = __builtin_amdgcn_readlane(my_j, t);
-      return kvb + ((int64_t)phys * c.Hp + j) * 2 * P * D;
+      return kvb + (phys >= 0 ? ((int64_t)phys * c.Hp + j) * 2 * P * D : 0);
     };
-    auto load_k = [&](const uint16_t* kt) {
+    auto load_k = [&](const uint16_t* kt, uint4 (&dst)[TL]) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) kr[kb] = ld16(kt + k_off + 32 * kb);
+      for (int k = 0; k < TL; ++k) dst[k] = ld16(kt + v_off + RPL * k * D);
     };
-    auto load_v = [&](const uint16_t* kt) {
+    auto load_v = [&](const uint16_t* kt, uint4 (&dst)[TL]) {
 #pragma unroll
-      for (int k = 0; k < TL; ++k) vr[k] = ld16(kt + P * D + v_off + RPL * k * D);
+      for (int k = 0; k < TL; ++k) dst[k] = ld16(kt + P * D + v_off + RPL * k * D);
     };
-    int next_phys = __builtin_amdgcn_readlane(my_phys, 0);
-    if (next_phys >= 0) {
-      const uint16_t* kt = tile(0);
-      load_k(kt);
-      load_v(kt);
+#pragma unroll
+    for (int b = 0; b < DEPTH; ++b) {
+      const uint16_t* kt = tile(b < nb ? b : nb - 1);
+      load_k(kt, kc[b]);
+      load_v(kt, vr[b]);
     }
-    for (int t = 0; t < nb; ++t) {
+    // One unit, its tiles in buffer B; refills buffer B with unit t + DEPTH.
+    auto unit = [&]<int B>(int t) {
       const int j = __builtin_amdgcn_readlane(my_j, t);
-      const int phys = next_phys;
+      const int phys = __builtin_amdgcn_readlane(my_phys, t);
       const int valid = __builtin_amdgcn_readlane(my_valid, t);
-      next_phys = t + 1 < nb ? __builtin_amdgcn_readlane(my_phys, t + 1) : -1;
       if (j != cur_j) {
         if (cur_j >= 0) end_head(cur_j);
         begin_head(j);
         cur_j = j;
       }
-      const uint16_t* nt = next_phys >= 0 ? tile(t + 1) : nullptr;
+      // tile to prefetch (past the batch end, the last unit re-reads its own:
+      // harmless, cached)
+      const uint16_t* nt = tile(t + DEPTH < nb ? t + DEPTH : nb - 1);
       if (phys < 0 || valid <= 0) {
-        if (nt) {
-          load_k(nt);
-          load_v(nt);
-        }
-        continue;
+        load_k(nt, kc[B]);
+        load_v(nt, vr[B]);
+        return;
       }
+      // K rows -> LDS, then back in MFMA operand layout (the global loads stay
+      // whole-row coalesced; the MFMA wants 16 rows x 64 B per operand).
+#pragma unroll
+      for (int k = 0; k < TL; ++k)
+        *reinterpret_cast<uint4*>(ktile + w_lds + RPL * k * KROW) = kc[B][k];
+      load_k(nt, kc[B]);   // K registers free: fetch a later unit's K
+      // The workgroup is one wave and a wave's LDS operations execute in
+      // order; the compiler barrier keeps the reads after the writes and the
+      // LDS-only wait (vmcnt, expcnt left at their maxima) leaves the
+      // prefetch loads in flight.
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      uint4 kr[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) kr[kb] = *reinterpret_cast<const uint4*>(ktile + k_lds + 32 * kb);
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) acc = mfma16x16x32(kr[kb], qop[kb], acc, DT());
-      if (nt) load_k(nt);   // K consumed: fetch the next unit's K
-
       // online softmax in the result layout (column rcol = query head)
       float z[4], tmax = -__builtin_inff();
 #pragma unroll
@@ -305,8 +367,8 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
       for (int k = 0; k < TL; ++k) {
         // rows past the valid count hold no token (possibly NaN): zero them
         const bool ok = rg + RPL * k < valid;
-        const uint32_t w[4] = {ok ? vr[k].x : 0u, ok ? vr[k].y : 0u, ok ? vr[k].z : 0u,
-                               ok ? vr[k].w : 0u};
+        const uint32_t w[4] = {ok ? vr[B][k].x : 0u, ok ? vr[B][k].y : 0u,
+                               ok ? vr[B][k].z : 0u, ok ? vr[B][k].w : 0u};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float v0 = lo_f(w[e], DT()), v1 = hi_f(w[e], DT());
@@ -317,51 +379,50 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
           }
         }
       }
-      if (nt) load_v(nt);   // V consumed: fetch the next unit's V
+      load_v(nt, vr[B]);   // V consumed: fetch a later unit's V
+    };
+    for (int t0 = 0; t0 < nb; t0 += DEPTH) {
+      [&]<int... B>(std::integer_sequence<int, B...>) {
+        ((t0 + B < nb ? unit.template operator()<B>(t0 + B) : void()), ...);
+      }(std::make_integer_sequence<int, DEPTH>{});
     }
   }
   if (cur_j >= 0) end_head(cur_j);
 }
 
-// Split that owns unit u when U units are cut into S ranges starting at
-// floor(s U / S): the largest s with floor(s U / S) <= u, i.e.
-// s = floor(((u + 1) S - 1) / U).
-__device__ __forceinline__ int split_of(int64_t u, int64_t U, int64_t S) {
-  return (int)(((u + 1) * S - 1) / U);
-}
-
 // One wave per (request, query head).  The splits that touched the head form
-// a contiguous range [s_lo, s_hi]; M = max lse and the weights 2^(lse - M)
-// are formed lane-parallel, then 8 splits are merged per step: lane l takes
-// split l / 8 of the step and channels (l % 8) * D/8 .. +D/8, and the 8 split
-// lanes of each channel chunk are summed with DPP / lane swaps at the end.
+// the contiguous range [first, last] that the decode kernel recorded (an
+// empty split inside it carries lse = -inf).  M = max lse and the weights
+// 2^(lse - M) are formed lane-parallel (lane = split), then 8 splits are
+// merged per step: lane l takes split l / 8 of the step (its weight comes by
+// shuffle) and channels (l % 8) * D/8 .. +D/8; the 8 split lanes of each
+// channel chunk are summed with DPP / lane swaps at the end.
 template <int D>
 __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a) {
   constexpr int CH = D / 8;          // channels per lane
   constexpr int V4 = CH / 4;         // float4 loads per split row
-  __shared__ GroupUnits gu;
   const CacheView& c = a.c;
   const int lane = threadIdx.x;
   const int r = blockIdx.x / c.Hq;
   const int g = blockIdx.x % c.Hq;
   const int h = g / c.Gq;
-  const int hs = c.head_slot[h];
+  const int64_t rh = (int64_t)r * c.Hkv + h;
   float* dst = a.out + ((int64_t)r * c.Hq + g) * D;
-  const int gi = (hs >= 0 && hs < c.Hkv) ? hs / c.Hp : 0, j = (hs >= 0 && hs < c.Hkv) ? hs % c.Hp : 0;
-  group_units(a, r, gi, &gu);
-  const int64_t U = gu.total;
-  const int64_t Si = a.S_prefix[gi + 1] - a.S_prefix[gi];
-  const bool live = hs >= 0 && hs < c.Hkv && gu.head[j] == h && gu.count[j] > 0;
-  const int s_lo = live ? split_of(gu.start[j], U, Si) : 0;
-  const int s_hi = live ? split_of(gu.start[j] + gu.count[j] - 1, U, Si) : -1;
+  // the head's unit count, exactly as the decode kernel forms it
+  const int n = clampi(c.seq_len[rh], 0, P * c.maxpg);
+  int cnt = (n + P - 1) / P;
+  if (a.sel) cnt = min(cnt, clampi(a.sel_count[rh], 0, a.K));
+  const int lo = a.split_lo[rh], hi = a.split_hi[rh];
+  const int s_lo = cnt > 0 ? clampi(lo, 0, a.Smax - 1) : 0;
+  const int s_hi = cnt > 0 ? clampi(hi, s_lo, a.Smax - 1) : -1;
   const int64_t row = ((int64_t)r * c.Hq + g) * a.Smax;
-  // A split whose unit range is empty wrote nothing (possible when U < S_i).
-  auto lse_of = [&](int s) {
-    const bool ok = s <= s_hi && (s * U) / Si < ((s + 1) * U) / Si;
-    return ok ? a.lse_part[row + s] : -__builtin_inff();
-  };
-  float M = -__builtin_inff();
-  for (int s = s_lo + lane; s <= s_hi; s += 64) M = fmaxf(M, lse_of(s));
+
+  float my_lse = -__builtin_inff(), M = -__builtin_inff();
+  for (int w0 = s_lo; w0 <= s_hi; w0 += 64) {
+    const float v = w0 + lane <= s_hi ? a.lse_part[row + w0 + lane] : -__builtin_inff();
+    if (w0 == s_lo) my_lse = v;
+    M = fmaxf(M, v);
+  }
   M = group_max<64>(M);
   float acc[CH];
 #pragma unroll
@@ -369,25 +430,33 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a) {
   float den = 0.f;
   const int sl = lane / 8, dc = lane % 8;
   if (M > -__builtin_inff()) {
-    for (int s0 = s_lo; s0 <= s_hi; s0 += 8) {
-      const int s = s0 + sl;
-      const float w = s <= s_hi ? __builtin_amdgcn_exp2f(lse_of(s) - M) : 0.f;
-      if (w > 0.f) {
-        den += w;
-        const float4* src = reinterpret_cast<const float4*>(a.o_part + (row + s) * D + dc * CH);
+    for (int w0 = s_lo; w0 <= s_hi; w0 += 64) {
+      const float lw = w0 == s_lo ? my_lse
+                                  : (w0 + lane <= s_hi ? a.lse_part[row + w0 + lane] : -__builtin_inff());
+      const float wt = __builtin_amdgcn_exp2f(lw - M);   // 0 for an empty split
+      den += wt;
+      const int nsp = min(64, s_hi - w0 + 1);
+#pragma unroll 2
+      for (int s8 = 0; s8 < nsp; s8 += 8) {
+        const int sp = s8 + sl;
+        const float w = __shfl(wt, sp, 64);
+        const bool ok = sp < nsp && w > 0.f;
+        // in-bounds row even when unused; an unused row may hold stale data,
+        // so its contribution is selected away, never multiplied in
+        const float4* src =
+            reinterpret_cast<const float4*>(a.o_part + (row + w0 + min(sp, nsp - 1)) * D + dc * CH);
 #pragma unroll
         for (int v = 0; v < V4; ++v) {
           const float4 x = src[v];
-          acc[4 * v] += w * x.x;
-          acc[4 * v + 1] += w * x.y;
-          acc[4 * v + 2] += w * x.z;
-          acc[4 * v + 3] += w * x.w;
+          acc[4 * v] += ok ? w * x.x : 0.f;
+          acc[4 * v + 1] += ok ? w * x.y : 0.f;
+          acc[4 * v + 2] += ok ? w * x.z : 0.f;
+          acc[4 * v + 3] += ok ? w * x.w : 0.f;
         }
       }
     }
   }
-  // sum over the 8 split lanes (lane bits 3..5) of each channel chunk
-  den = group_sum<64>(den) * (1.f / 8.f);   // every split lane counted each weight once; dc copies x8
+  den = group_sum<64>(den);   // each split's weight is held by one lane
 #pragma unroll
   for (int e = 0; e < CH; ++e) {
     float v = acc[e];

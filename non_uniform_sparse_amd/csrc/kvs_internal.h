@@ -41,6 +41,9 @@ struct DecodeArgs {
   float scale_log2;          // softmax scale * log2(e): logits kept in base 2
   float* o_part;             // [b][Hq][Smax][d]
   float* lse_part;           // [b][Hq][Smax], base-2 log-sum-exp
+  int32_t* split_lo;         // [b][Hkv] first split touching each head
+  int32_t* split_hi;         // [b][Hkv] last split touching each head
+  uint64_t* stamps;          // instrumented build only: [b * splits_total][2] start/end
   int Smax;                  // max_i S_i
   int splits_total;          // sum_i S_i
   float* out;                // [b][Hq][d]

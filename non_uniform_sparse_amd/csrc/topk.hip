@@ -1,15 +1,16 @@
 // Per-KV-head top-K page selection (FlexiCache summary, Core method: each
-// head attends only its K best pages).  One wave per (request, head).
-// Scores become order-preserving 32-bit keys held in LDS; a most-significant-
-// digit radix select (4 passes of 8 bits) finds the K-th largest key tau:
-// a pass whose candidate keys (those matching the digits chosen so far) all
-// share one digit takes it directly; otherwise it builds a 256-bin LDS
-// histogram of the candidates, every lane owns 4 bins, a suffix scan over lanes gives the
-// count above each lane's bins and the one lane whose bins straddle the K-th
-// key publishes the digit.  Pages with key > tau are kept, and among pages
-// with key == tau the lowest page indices fill the remaining places; ballots
-// over 64-page windows rank the ties and place the kept pages in ascending
-// page order.  Integer work only, so the result is deterministic.
+// head attends only its K best pages).  One 256-thread workgroup per
+// (request, head).  Scores become order-preserving 32-bit keys held in LDS;
+// a most-significant-digit radix select (4 passes of 8 bits) finds the K-th
+// largest key tau.  A pass whose candidate keys (those matching the digits
+// chosen so far) all share one digit takes it directly; otherwise it builds a
+// 256-bin LDS histogram of the candidates, one wave owns the bins (4 per
+// lane), a suffix scan over its lanes gives the count above each lane's bins
+// and the one lane whose bins straddle the K-th key publishes the digit.
+// Pages with key > tau are kept, and among pages with key == tau the lowest
+// page indices fill the remaining places; ballots and per-wave counts over
+// 256-page windows rank the ties and place the kept pages in ascending page
+// order.  Integer work only, so the result is deterministic.
 #include "kvs_device.h"
 
 namespace kvs {
@@ -28,30 +29,58 @@ __device__ __forceinline__ int rank_below(uint64_t m) {
                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-__global__ __launch_bounds__(64) void topk_kernel(const float* __restrict__ scores,
-                                                  const int32_t* __restrict__ seq_len, int P,
-                                                  int max_pages, int K, int32_t* __restrict__ sel,
-                                                  int32_t* __restrict__ sel_count) {
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+// Block-wide min and max of one int per thread (every thread gets both).
+__device__ __forceinline__ void block_minmax(int lo, int hi, int* red, int* out_lo, int* out_hi) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  lo = -(int)group_max<64>(-(float)lo);
+  hi = (int)group_max<64>((float)hi);
+  if (lane == 0) {
+    red[wid] = lo;
+    red[kWaves + wid] = hi;
+  }
+  __syncthreads();
+  int a = red[0], b = red[kWaves];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) {
+    a = min(a, red[w]);
+    b = max(b, red[kWaves + w]);
+  }
+  __syncthreads();
+  *out_lo = a;
+  *out_hi = b;
+}
+
+__global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ scores,
+                                                        const int32_t* __restrict__ seq_len, int P,
+                                                        int max_pages, int K,
+                                                        int32_t* __restrict__ sel,
+                                                        int32_t* __restrict__ sel_count) {
   extern __shared__ uint32_t keys[];   // [max_pages]
   __shared__ int hist[256];
+  __shared__ int red[2 * kWaves];
+  __shared__ int s_digit, s_need;
   const int rh = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int n = clampi(seq_len[rh], 0, P * max_pages);
   const int npg = (n + P - 1) / P;
   const int keep = min(K, npg);
   const float* row = scores + (int64_t)rh * max_pages;
   int32_t* out = sel + (int64_t)rh * K;
 
-  for (int p = lane; p < npg; p += 64) keys[p] = order_key(row[p]);
+  for (int p = tid; p < npg; p += kThreads) keys[p] = order_key(row[p]);
+  __syncthreads();
 
   uint32_t prefix = 0, mask = 0;
   int need = keep;   // keys equal to the final prefix still to take
   for (int shift = 24; shift >= 0 && keep > 0; shift -= 8) {
     // Scores of one head often share their top bits: if every candidate key
-    // has the same digit, it is the digit, with no histogram (and no
-    // 64-way atomic contention on one bin).
+    // has the same digit, it is the digit, with no histogram (and no atomic
+    // contention on one bin).
     int dmin = 256, dmax = -1;
-    for (int p = lane; p < npg; p += 64) {
+    for (int p = tid; p < npg; p += kThreads) {
       const uint32_t k = keys[p];
       if ((k & mask) == prefix) {
         const int dg = (int)((k >> shift) & 255u);
@@ -59,68 +88,90 @@ __global__ __launch_bounds__(64) void topk_kernel(const float* __restrict__ scor
         dmax = max(dmax, dg);
       }
     }
-    dmin = (int)group_max<64>(-(float)dmin) * -1;
-    dmax = (int)group_max<64>((float)dmax);
+    block_minmax(dmin, dmax, red, &dmin, &dmax);
     if (dmin == dmax) {
       prefix |= (uint32_t)dmin << shift;
       mask |= 255u << shift;
       continue;
     }
-    for (int b = lane; b < 256; b += 64) hist[b] = 0;
+    hist[tid] = 0;   // kThreads == 256 bins
     __syncthreads();
-    for (int p = lane; p < npg; p += 64) {
+    for (int p = tid; p < npg; p += kThreads) {
       const uint32_t k = keys[p];
       if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1);
     }
     __syncthreads();
-    int hb[4], mine = 0;
+    if (wid == 0) {
+      int hb[4], mine = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      hb[i] = hist[4 * lane + i];
-      mine += hb[i];
-    }
-    // inclusive suffix sum over lanes (lane 63 holds the largest digits)
-    int incl = mine;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int t = __shfl_down(incl, off, 64);
-      if (lane + off < 64) incl += t;
-    }
-    int acc = incl - mine;   // keys in bins above this lane's
-    int found = -1, left = 0;
-#pragma unroll
-    for (int i = 3; i >= 0; --i) {
-      if (found < 0 && acc < need && need <= acc + hb[i]) {
-        found = 4 * lane + i;
-        left = need - acc;
+      for (int i = 0; i < 4; ++i) {
+        hb[i] = hist[4 * lane + i];
+        mine += hb[i];
       }
-      acc += hb[i];
+      // inclusive suffix sum over lanes (lane 63 holds the largest digits)
+      int incl = mine;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_down(incl, off, 64);
+        if (lane + off < 64) incl += t;
+      }
+      int acc = incl - mine;   // keys in bins above this lane's
+      int found = -1, left = 0;
+#pragma unroll
+      for (int i = 3; i >= 0; --i) {
+        if (found < 0 && acc < need && need <= acc + hb[i]) {
+          found = 4 * lane + i;
+          left = need - acc;
+        }
+        acc += hb[i];
+      }
+      if (found >= 0) {   // exactly one lane
+        s_digit = found;
+        s_need = left;
+      }
     }
-    const uint64_t who = __ballot(found >= 0);
-    const int src = __builtin_ctzll(who);
-    prefix |= (uint32_t)__shfl(found, src, 64) << shift;
-    need = __shfl(left, src, 64);
+    __syncthreads();
+    prefix |= (uint32_t)s_digit << shift;
+    need = s_need;
     mask |= 255u << shift;
     __syncthreads();
   }
   const uint32_t tau = prefix;
   const int ties = need;
 
+  // Windows of 256 pages in page order: rank ties, then place kept pages.
   int eq_before = 0, pos_before = 0;
-  for (int base = 0; base < npg; base += 64) {
-    const int p = base + lane;
+  for (int base = 0; base < npg; base += kThreads) {
+    const int p = base + tid;
     const uint32_t k = p < npg ? keys[p] : 0u;
     const bool eq = p < npg && k == tau;
     const uint64_t eqm = __ballot(eq);
-    const bool take = keep > 0 && p < npg && (k > tau || (eq && eq_before + rank_below(eqm) < ties));
+    if (lane == 0) red[wid] = __popcll(eqm);
+    __syncthreads();
+    int eq_w = eq_before, eq_all = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      eq_w += w < wid ? red[w] : 0;
+      eq_all += red[w];
+    }
+    const bool take = keep > 0 && p < npg && (k > tau || (eq && eq_w + rank_below(eqm) < ties));
     const uint64_t tm = __ballot(take);
-    const int pos = pos_before + rank_below(tm);
+    if (lane == 0) red[kWaves + wid] = __popcll(tm);
+    __syncthreads();
+    int pos = pos_before, t_all = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      pos += w < wid ? red[kWaves + w] : 0;
+      t_all += red[kWaves + w];
+    }
+    pos += rank_below(tm);
     if (take && pos < keep) out[pos] = p;
-    eq_before += __popcll(eqm);
-    pos_before += __popcll(tm);
+    eq_before += eq_all;
+    pos_before += t_all;
+    __syncthreads();
   }
-  for (int k = keep + lane; k < K; k += 64) out[k] = -1;
-  if (lane == 0) sel_count[rh] = keep;
+  for (int k = keep + tid; k < K; k += kThreads) out[k] = -1;
+  if (tid == 0) sel_count[rh] = keep;
 }
 
 }  // namespace
@@ -128,7 +179,7 @@ __global__ __launch_bounds__(64) void topk_kernel(const float* __restrict__ scor
 hipError_t launch_topk(const float* scores, const int32_t* seq_len, int P, int b, int Hkv,
                        int max_pages, int K, int32_t* sel, int32_t* sel_count, hipStream_t s) {
   const size_t lds = (size_t)max_pages * sizeof(uint32_t);
-  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)(b * Hkv)), dim3(64), lds, s, scores, seq_len, P,
+  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)(b * Hkv)), dim3(kThreads), lds, s, scores, seq_len, P,
                      max_pages, K, sel, sel_count);
   return hipGetLastError();
 }

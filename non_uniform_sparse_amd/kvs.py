@@ -53,6 +53,15 @@ class PagedKV(ctypes.Structure):
 _lib = None
 
 
+def use_library(path: str) -> None:
+    """Select which build of the library to load (before its first use), e.g.
+    the workgroup-stamp instrumented one for skew measurements."""
+    global LIB_PATH
+    if _lib is not None:
+        raise RuntimeError("library already loaded")
+    LIB_PATH = path
+
+
 def lib() -> ctypes.CDLL:
     """Load libkvs.so (built in-tree by ``python -m non_uniform_sparse_amd.build``)."""
     global _lib
@@ -68,11 +77,14 @@ def lib() -> ctypes.CDLL:
         L.kvs_topk_pages.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
         L.kvs_plan_split.argtypes = [vp, vp, i32, i32, i32, f64, i32, vp]
         L.kvs_decode_attn.argtypes = [pkv, vp, vp, vp, i32, vp, f32, vp, ctypes.c_size_t, vp, vp]
-        L.kvs_decode_workspace_bytes.argtypes = [i32, i32, i32, vp, i32]
+        L.kvs_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, vp, i32]
         L.kvs_decode_workspace_bytes.restype = ctypes.c_size_t
         L.kvs_decode_concurrency.argtypes = [i32, i32, i32, i32, vp]
         L.kvs_cluster_heads.argtypes = [vp, i32, i32, i32, vp]
         L.kvs_last_error.restype = ctypes.c_char_p
+        if hasattr(L, "kvs_decode_stamps_offset"):   # instrumented build only
+            L.kvs_decode_stamps_offset.argtypes = [i32, i32, i32, i32, vp, i32]
+            L.kvs_decode_stamps_offset.restype = ctypes.c_size_t
         for name in EXPORTS:
             if name not in ("kvs_decode_workspace_bytes", "kvs_last_error"):
                 getattr(L, name).restype = ctypes.c_int
@@ -179,9 +191,9 @@ def kvs_cluster_heads(budgets: np.ndarray, Hp: int) -> np.ndarray:
     return hs
 
 
-def kvs_decode_workspace_bytes(b: int, Hq: int, d: int, S_row: Sequence[int]) -> int:
+def kvs_decode_workspace_bytes(b: int, Hq: int, Hkv: int, d: int, S_row: Sequence[int]) -> int:
     S = np.ascontiguousarray(S_row, dtype=np.int32)
-    return int(lib().kvs_decode_workspace_bytes(b, Hq, d, S.ctypes.data, len(S)))
+    return int(lib().kvs_decode_workspace_bytes(b, Hq, Hkv, d, S.ctypes.data, len(S)))
 
 
 def kvs_decode_attn(cache: Cache, q: torch.Tensor, sel: Optional[torch.Tensor],
@@ -209,3 +221,10 @@ def kvs_decode_concurrency(device: int, d: int, gqa: int, dtype: torch.dtype) ->
     W = ctypes.c_int32(0)
     _check(lib().kvs_decode_concurrency(device, d, gqa, dtype_code(dtype), ctypes.byref(W)))
     return W.value
+
+
+def kvs_decode_stamps_offset(b: int, Hq: int, Hkv: int, d: int, S_row: Sequence[int]) -> int:
+    """Instrumented build only: byte offset of the per-workgroup [start, end]
+    uint64 stamps inside the decode workspace."""
+    S = np.ascontiguousarray(S_row, dtype=np.int32)
+    return int(lib().kvs_decode_stamps_offset(b, Hq, Hkv, d, S.ctypes.data, len(S)))

@@ -75,7 +75,7 @@ class DecodeStep:
         self.S = np.asarray(S, dtype=np.int32)
         self.T = int(self.S[0].sum())
         self.scale = 1.0 / math.sqrt(c.d)
-        ws = max(kvs.kvs_decode_workspace_bytes(c.b, c.Hq, c.d, row) for row in self.S)
+        ws = max(kvs.kvs_decode_workspace_bytes(c.b, c.Hq, c.Hkv, c.d, row) for row in self.S)
         self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
         self.bufs: List[LayerBuffers] = []
         for l in range(c.L):
@@ -114,3 +114,19 @@ class DecodeStep:
     def run(self, qs: List[torch.Tensor], stream=None) -> None:
         for l in range(self.cfg.L):
             self.run_layer(l, qs[l], stream)
+
+    def capture(self, qs: List[torch.Tensor]) -> "torch.cuda.CUDAGraph":
+        """Record one whole step (every layer) as a HIP graph.  Every launch
+        has a static grid and takes its arguments by value, and the step
+        issues no memset, so a replay re-runs exactly the eager step on the
+        buffers bound at capture time."""
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.run(qs, side)          # warm-up on the capture stream
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            self.run(qs, torch.cuda.current_stream())
+        return g

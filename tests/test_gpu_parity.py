@@ -70,7 +70,7 @@ def test_split_invariance(name):
     outs = {}
     c = wl.cfg
     for key, row in _split_rows(step, 0).items():
-        need = kvs.kvs_decode_workspace_bytes(c.b, c.Hq, c.d, row)
+        need = kvs.kvs_decode_workspace_bytes(c.b, c.Hq, c.Hkv, c.d, row)
         if need > step.workspace.numel():
             step.workspace = torch.empty(need, dtype=torch.uint8, device="cuda")
         outs[key] = step.attend(0, q, S_row=row).clone()
@@ -140,3 +140,31 @@ def test_deterministic():
     b = step.run_layer(0, q).clone()
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(sel_a, step.bufs[0].sel)
+
+
+@pytest.mark.parametrize("name", ["flexicache_topk", "longctx_skew"])
+def test_graph_replay_matches_eager(name):
+    """A captured step replays to the eager result, every replay, with eager
+    work and synchronisation in between."""
+    ov = {"b": 6} if name == "flexicache_topk" else {"L": 3}
+    wl, step = _full(name, **ov)
+    qs = step.queries()
+    step.run(qs)
+    torch.cuda.synchronize()
+    ref = [b.out.clone() for b in step.bufs]
+    ref_sel = [b.sel.clone() if b.sel is not None else None for b in step.bufs]
+    g = step.capture(qs)
+    for rep in range(3):
+        for b in step.bufs:
+            b.out.fill_(float("nan"))
+            if b.sel is not None:
+                b.sel.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for l, b in enumerate(step.bufs):
+            assert torch.equal(b.out, ref[l]), f"replay {rep} layer {l}"
+            if b.sel is not None:
+                assert torch.equal(b.sel, ref_sel[l])
+        step.run(qs)                 # eager work between replays
+        torch.cuda.synchronize()

@@ -159,8 +159,8 @@ def test_decode_validation():
     L = _lib()
     s = _FakeCache().s
     S = np.array([2, 2], dtype=np.int32)
-    need = kvs.kvs_decode_workspace_bytes(1, 32, 128, S)
-    assert need == 1 * 32 * 2 * 128 * 4 + 256
+    need = kvs.kvs_decode_workspace_bytes(1, 32, 8, 128, S)
+    assert need == 1 * 32 * 2 * 128 * 4 + 256 + 2 * 256
     args = lambda **k: [ctypes.byref(s), k.get("q", 0x60000), k.get("sel", None), k.get("cnt", None),
                         k.get("K", 0), k.get("S", S).ctypes.data, ctypes.c_float(k.get("scale", 0.088)),
                         k.get("ws", 0x100000), k.get("wsb", need), k.get("out", 0x80000), None]
