@@ -74,6 +74,20 @@ def algorithmic_bytes(step: DecodeStep, l: int) -> dict:
             "decode_launch": kv + rows * (c.d + 1) * 4 * 2 + c.b * c.Hq * c.d * (s + 4)}
 
 
+def stored_traffic(workload: str):
+    """HBM bytes per kvs_decode_attn launch from the committed rocprofv3 PMC
+    record of this workload (FETCH_SIZE and WRITE_SIZE, scaled by a copy of
+    known size), or None if there is none or the decode source changed since."""
+    from non_uniform_sparse_amd import profiling
+    path = os.path.join(ROOT, "profiles", f"decode_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha256") != profiling.decode_source_hash():
+        return None
+    return rec["traffic_bytes_per_launch"]
+
+
 def cpu_baseline(wl, step, budget_s: float = 12.0) -> dict:
     """The fp64 oracle timed on this host on a bounded sample of the same
     workload: whole heads (score + top-K + attention; min-max metadata
@@ -279,6 +293,7 @@ def main() -> int:
     dec_bytes = statistics.mean(a["decode_launch"] for a in ab)
     achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
     value = kv_bytes / (ms * 1e-3) / 1e9
+    traffic = stored_traffic(c.name)
     rec = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -311,7 +326,7 @@ def main() -> int:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": traffic,
         },
         "wall_ms_per_step_incl_flush": round(wall_ms / args.steps, 4),
     }

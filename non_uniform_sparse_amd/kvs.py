@@ -228,3 +228,4 @@ def kvs_decode_stamps_offset(b: int, Hq: int, Hkv: int, d: int, S_row: Sequence[
     uint64 stamps inside the decode workspace."""
     S = np.ascontiguousarray(S_row, dtype=np.int32)
     return int(lib().kvs_decode_stamps_offset(b, Hq, Hkv, d, S.ctypes.data, len(S)))
+

@@ -168,3 +168,4 @@ def test_graph_replay_matches_eager(name):
                 assert torch.equal(b.sel, ref_sel[l])
         step.run(qs)                 # eager work between replays
         torch.cuda.synchronize()
+

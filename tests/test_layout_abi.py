@@ -203,3 +203,4 @@ def test_plan_validation():
         kvs.kvs_plan_split(np.ones((1, 8)), hs, 3, 0.0, 4)          # Hkv % Hp
     with pytest.raises(kvs.KvsError):
         kvs.kvs_cluster_heads(np.full((1, 8), 1.5), 4)
+
