@@ -64,10 +64,11 @@ enum { KVS_F16 = 0, KVS_BF16 = 1 };
  * the group leave the tail of their slots unused.
  *
  *   kv          device, [num_pages][Hp][2][P][d] dtype.
- *   minmax      device, [num_pages][Hp][2][d] dtype: per page and slot, the
- *               per-channel minimum (row 0) and maximum (row 1) of the valid
- *               keys [F Key observations, assumption 2].  Written by
- *               kvs_build_minmax, read by kvs_score_pages.
+ *   minmax      device, [num_pages][Hp][d][2] dtype: per page and slot, for
+ *               each channel the minimum (index 0) then the maximum (index 1)
+ *               of the valid keys [F Key observations, assumption 2].
+ *               Channel-interleaved so a head's page is one contiguous 4*d-byte
+ *               block.  Written by kvs_build_minmax, read by kvs_score_pages.
  *   page_table  device, [b][G][max_group_pages] int32 physical page ids;
  *               -1 marks a null entry [F System engineering].  Logical page
  *               p of head h covers its tokens [p*P, (p+1)*P).
@@ -94,7 +95,7 @@ typedef struct kvs_paged_kv {
 /*
  * Build the min-max page metadata [F Key observations, assumption 2; Core
  * method].  For every request r, head h and logical page p < ceil(n/P):
- * minmax[page][slot][0][c] = min and [1][c] = max over the page's valid
+ * minmax[page][slot][c][0] = min and [c][1] = max over the page's valid
  * tokens t in [p*P, min(n, (p+1)*P)) of K[t][c].  Exact (a selection).
  * Entries of slots or pages beyond a head's n are left untouched.
  * Runs once per page fill, not per decode step.

@@ -5,7 +5,9 @@
 // rows of d contiguous elements; lane l reads 16 bytes (8 channels) of row
 // rg + RPL*k, rg = l / COLS, so each load instruction covers RPL whole rows
 // (1 KB) and the tile is read once, fully coalesced.  Per-channel min/max
-// over the lane's rows, then across the RPL row groups with lane shuffles.
+// over the lane's rows, then across the RPL row groups with lane swaps.  The
+// output is channel-interleaved, (min, max) per channel, so that one page of
+// one head is a single contiguous 4*d-byte block for the scoring kernel.
 #include "kvs_device.h"
 
 namespace kvs {
@@ -64,18 +66,19 @@ __global__ __launch_bounds__(256) void minmax_kernel(CacheView c) {
     hi[e] = across_max<COLS>(hi[e]);
   }
   if (rg == 0) {
+    // channel-interleaved: (min, max) of channel ch at elements 2 ch, 2 ch + 1
     uint16_t* mm = reinterpret_cast<uint16_t*>(c.minmax) + ((int64_t)phys * c.Hp + slot) * 2 * D;
     uint4 a, b;
-    a.x = pack2(lo[0], lo[1], DT());
-    a.y = pack2(lo[2], lo[3], DT());
-    a.z = pack2(lo[4], lo[5], DT());
-    a.w = pack2(lo[6], lo[7], DT());
-    b.x = pack2(hi[0], hi[1], DT());
-    b.y = pack2(hi[2], hi[3], DT());
-    b.z = pack2(hi[4], hi[5], DT());
-    b.w = pack2(hi[6], hi[7], DT());
-    *reinterpret_cast<uint4*>(mm + 8 * col) = a;
-    *reinterpret_cast<uint4*>(mm + D + 8 * col) = b;
+    a.x = pack2(lo[0], hi[0], DT());
+    a.y = pack2(lo[1], hi[1], DT());
+    a.z = pack2(lo[2], hi[2], DT());
+    a.w = pack2(lo[3], hi[3], DT());
+    b.x = pack2(lo[4], hi[4], DT());
+    b.y = pack2(lo[5], hi[5], DT());
+    b.z = pack2(lo[6], hi[6], DT());
+    b.w = pack2(lo[7], hi[7], DT());
+    *reinterpret_cast<uint4*>(mm + 16 * col) = a;
+    *reinterpret_cast<uint4*>(mm + 16 * col + 8) = b;
   }
 }
 

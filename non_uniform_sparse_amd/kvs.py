@@ -128,7 +128,7 @@ def _need(t: torch.Tensor, name: str, shape, dtype, device=None) -> None:
 class Cache:
     """One layer's paged KV as device tensors (the fields of kvs_paged_kv)."""
     kv: torch.Tensor            # [num_pages][Hp][2][P][d]
-    minmax: torch.Tensor        # [num_pages][Hp][2][d]
+    minmax: torch.Tensor        # [num_pages][Hp][d][2]
     page_table: torch.Tensor    # int32 [b][G][max_group_pages]
     seq_len: torch.Tensor       # int32 [b][Hkv]
     head_slot: torch.Tensor     # int32 [Hkv]
@@ -140,7 +140,7 @@ class Cache:
         Hkv = self.seq_len.shape[1]
         dev = self.kv.device
         _need(self.kv, "kv", (num_pages, Hp, 2, P, d), self.kv.dtype, dev)
-        _need(self.minmax, "minmax", (num_pages, Hp, 2, d), self.kv.dtype, dev)
+        _need(self.minmax, "minmax", (num_pages, Hp, d, 2), self.kv.dtype, dev)
         _need(self.page_table, "page_table", (b, Hkv // Hp, maxpg), torch.int32, dev)
         _need(self.seq_len, "seq_len", (b, Hkv), torch.int32, dev)
         _need(self.head_slot, "head_slot", (Hkv,), torch.int32, dev)

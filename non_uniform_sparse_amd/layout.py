@@ -108,7 +108,7 @@ def build_caches(wl: Workload, head_slot: np.ndarray, device="cuda", poison: boo
                     k = int(need[l, r, i])
                     pt[r, i, :k] = pages(r, i)[:k]
             seq = wl.n[:, l, :].astype(np.int32)
-            mm = torch.empty((total, Hp, 2, d), dtype=dt, device=device)
+            mm = torch.empty((total, Hp, d, 2), dtype=dt, device=device)
             if poison:
                 _nan_fill(mm)
             caches[l] = Cache(kv=kv, minmax=mm,

@@ -99,10 +99,10 @@ def check_layer(step: DecodeStep, l: int, q: torch.Tensor, requests: Sequence[in
             lo, hi = O.page_minmax(K64, c.P)
             if check_minmax or c.topk:
                 ids = torch.as_tensor(lay.page_table[r, gi, :npg].astype(np.int64), device=dev)
-                g_mm = mm[ids, j].double().cpu().numpy()         # [npg][2][d]
+                g_mm = mm[ids, j].double().cpu().numpy()         # [npg][d][2]
                 if check_minmax:
-                    assert np.array_equal(g_mm[:, 0], lo), f"kmin r={r} l={l} h={h}"
-                    assert np.array_equal(g_mm[:, 1], hi), f"kmax r={r} l={l} h={h}"
+                    assert np.array_equal(g_mm[:, :, 0], lo), f"kmin r={r} l={l} h={h}"
+                    assert np.array_equal(g_mm[:, :, 1], hi), f"kmax r={r} l={l} h={h}"
                     stats.minmax_checked += npg
             qg = q64[r, h * c.Gq:(h + 1) * c.Gq]
             if c.topk:
