@@ -26,11 +26,12 @@
  *   - Layout is row-major C order throughout.  Element types: KV, min-max
  *     and queries are fp16 or bf16 (`dtype`), scores and outputs fp32,
  *     indices int32.  Device pointers must be 16-byte aligned.
- *   - Contents of device-resident integer inputs (seq_len, page_table, sel)
- *     cannot be checked before launch.  Kernels never read outside the
- *     buffers described here: a page id outside [0, num_pages) or a
- *     negative id is treated as a null page and skipped; seq_len is clamped
- *     to [0, P*max_group_pages]; sel_count is clamped to [0, K].
+ *   - Contents of device-resident integer inputs (seq_len, page_table,
+ *     meta_base, sel) cannot be checked before launch.  Kernels never read
+ *     outside the buffers described here: a page id outside [0, num_pages)
+ *     or a negative id is treated as a null page and skipped, as is a
+ *     min-max block outside [0, num_meta); seq_len is clamped to
+ *     [0, P*max_group_pages]; sel_count is clamped to [0, K].
  */
 #ifndef KVS_H_
 #define KVS_H_
@@ -64,11 +65,16 @@ enum { KVS_F16 = 0, KVS_BF16 = 1 };
  * the group leave the tail of their slots unused.
  *
  *   kv          device, [num_pages][Hp][2][P][d] dtype.
- *   minmax      device, [num_pages][Hp][d][2] dtype: per page and slot, for
- *               each channel the minimum (index 0) then the maximum (index 1)
- *               of the valid keys [F Key observations, assumption 2].
- *               Channel-interleaved so a head's page is one contiguous 4*d-byte
- *               block.  Written by kvs_build_minmax, read by kvs_score_pages.
+ *   minmax      device, [num_meta][d][2] dtype: the min-max cache [F Key
+ *               observations, assumption 2], kept apart from the KV pages
+ *               and ragged per head: block meta_base[r][h] + p holds, for
+ *               logical page p of head h of request r, per channel the
+ *               minimum (index 0) then the maximum (index 1) of the valid
+ *               keys.  A head's bounds are one contiguous run in page order
+ *               however its KV pages are scattered.  Written by
+ *               kvs_build_minmax, read by kvs_score_pages.
+ *   meta_base   device, [b][Hkv] int32: first minmax block of each head; the
+ *               head's run holds ceil(n/P) blocks.
  *   page_table  device, [b][G][max_group_pages] int32 physical page ids;
  *               -1 marks a null entry [F System engineering].  Logical page
  *               p of head h covers its tokens [p*P, (p+1)*P).
@@ -79,6 +85,7 @@ enum { KVS_F16 = 0, KVS_BF16 = 1 };
  *               slot head_slot[h]%Hp; a permutation of [0, Hkv).
  *   b, Hq, Hkv  requests, query heads, KV heads (Hq % Hkv == 0).
  *   Hp          heads per page group (Hkv % Hp == 0, G <= 64).
+ *   num_meta    blocks in minmax.
  *   d           head dimension: 128 or 256.
  *   P           tokens per page: 16.
  *   dtype       KVS_F16 or KVS_BF16.
@@ -86,18 +93,21 @@ enum { KVS_F16 = 0, KVS_BF16 = 1 };
 typedef struct kvs_paged_kv {
   const void* kv;
   void* minmax;
+  const int32_t* meta_base;
   const int32_t* page_table;
   const int32_t* seq_len;
   const int32_t* head_slot;
-  int32_t b, Hq, Hkv, Hp, d, P, max_group_pages, num_pages, dtype;
+  int32_t b, Hq, Hkv, Hp, d, P, max_group_pages, num_pages, num_meta, dtype;
 } kvs_paged_kv;
 
 /*
  * Build the min-max page metadata [F Key observations, assumption 2; Core
  * method].  For every request r, head h and logical page p < ceil(n/P):
- * minmax[page][slot][c][0] = min and [c][1] = max over the page's valid
- * tokens t in [p*P, min(n, (p+1)*P)) of K[t][c].  Exact (a selection).
- * Entries of slots or pages beyond a head's n are left untouched.
+ * minmax[meta_base[r][h] + p][c][0] = min and [c][1] = max over the page's
+ * valid tokens t in [p*P, min(n, (p+1)*P)) of K[t][c].  Exact (a
+ * selection).  Pages with a null table entry and block indices outside
+ * [0, num_meta) are skipped.
+ * Blocks of pages beyond a head's n are left untouched.
  * Runs once per page fill, not per decode step.
  */
 int kvs_build_minmax(const kvs_paged_kv* cache, void* stream);
@@ -108,9 +118,12 @@ int kvs_build_minmax(const kvs_paged_kv* cache, void* stream);
  *   scores[r][h][p] = max over the Gq query heads g of h of
  *                     sum_c max(q[r][g][c]*kmin[c], q[r][g][c]*kmax[c])
  * (no 1/sqrt(d) scale), fp32 products of the fp16/bf16 inputs (exact) summed
- * in a fixed order.  Pages p >= ceil(n/P) get -inf.
+ * in a fixed order.  Pages p >= ceil(n/P), pages with a null table entry and
+ * pages whose block is outside [0, num_meta) get -inf.
  *   q       device, [b][Hq][d] dtype; query head g belongs to KV head g/Gq.
  *   scores  device, [b][Hkv][max_group_pages] fp32, fully written.
+ * Supported sizes: b*Hkv <= 16383 and b*Hkv*max_group_pages < 2^31
+ * (KVS_EUNSUPPORTED otherwise).
  */
 int kvs_score_pages(const kvs_paged_kv* cache, const void* q, float* scores, void* stream);
 

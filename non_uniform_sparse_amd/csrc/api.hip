@@ -20,8 +20,11 @@ int hip_error(hipError_t e, const char* what) {
 // Validates the cache descriptor.  need_minmax: the call reads or writes it.
 int check_cache(const kvs_paged_kv* p, bool need_minmax, const char* fn, CacheView* v) {
   if (!p) return set_error(KVS_EINVAL, "%s: cache descriptor is NULL", fn);
-  if (!p->kv || !p->page_table || !p->seq_len || !p->head_slot || (need_minmax && !p->minmax))
+  if (!p->kv || !p->page_table || !p->seq_len || !p->head_slot ||
+      (need_minmax && (!p->minmax || !p->meta_base)))
     return set_error(KVS_EINVAL, "%s: null device pointer in cache descriptor", fn);
+  if (need_minmax && p->num_meta < 1)
+    return set_error(KVS_EINVAL, "%s: num_meta must be positive", fn);
   if (!aligned16(p->kv) || (need_minmax && !aligned16(p->minmax)))
     return set_error(KVS_EINVAL, "%s: kv and minmax must be 16-byte aligned", fn);
   if (p->b < 1 || p->Hkv < 1 || p->Hq < 1 || p->Hp < 1 || p->max_group_pages < 1 ||
@@ -45,6 +48,8 @@ int check_cache(const kvs_paged_kv* p, bool need_minmax, const char* fn, CacheVi
     return set_error(KVS_EINVAL, "%s: cache too large", fn);
   v->kv = p->kv;
   v->minmax = p->minmax;
+  v->meta_base = p->meta_base;
+  v->num_meta = p->num_meta;
   v->page_table = p->page_table;
   v->seq_len = p->seq_len;
   v->head_slot = p->head_slot;
@@ -110,6 +115,11 @@ extern "C" int kvs_score_pages(const kvs_paged_kv* cache, const void* q, float* 
   if (int rc = check_cache(cache, true, "kvs_score_pages", &c)) return rc;
   if (!q || !scores) return set_error(KVS_EINVAL, "kvs_score_pages: null q or scores");
   if (!aligned16(q)) return set_error(KVS_EINVAL, "kvs_score_pages: q must be 16-byte aligned");
+  if ((int64_t)c.b * c.Hkv > kMaxScoreHeads)
+    return set_error(KVS_EUNSUPPORTED, "kvs_score_pages: b*Hkv=%lld > %d", (long long)c.b * c.Hkv,
+                     kMaxScoreHeads);
+  if ((int64_t)c.b * c.Hkv * c.maxpg > 0x7fffffff)
+    return set_error(KVS_EUNSUPPORTED, "kvs_score_pages: b*Hkv*max_group_pages >= 2^31");
   if (hipError_t e = launch_score(c, q, scores, (hipStream_t)stream))
     return hip_error(e, "kvs_score_pages");
   return KVS_OK;

@@ -16,6 +16,7 @@ constexpr int kMaxHkv = 128;
 constexpr int kMaxTopkPages = 8192;
 constexpr int kMaxK = 1024;
 constexpr int kMaxSplitsPerRequest = 65536;
+constexpr int kMaxScoreHeads = 16383;   // b * Hkv: page-count prefix held in 64 KB of LDS
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Records a message for kvs_last_error() and returns `code`.
@@ -26,10 +27,11 @@ void clear_error();
 struct CacheView {
   const void* kv;
   void* minmax;
+  const int32_t* meta_base;
   const int32_t* page_table;
   const int32_t* seq_len;
   const int32_t* head_slot;
-  int b, Hq, Hkv, Hp, G, Gq, d, P, maxpg, num_pages, dtype;
+  int b, Hq, Hkv, Hp, G, Gq, d, P, maxpg, num_pages, num_meta, dtype;
 };
 
 struct DecodeArgs {

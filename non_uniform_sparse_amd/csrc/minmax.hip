@@ -7,7 +7,9 @@
 // (1 KB) and the tile is read once, fully coalesced.  Per-channel min/max
 // over the lane's rows, then across the RPL row groups with lane swaps.  The
 // output is channel-interleaved, (min, max) per channel, so that one page of
-// one head is a single contiguous 4*d-byte block for the scoring kernel.
+// one head is a single contiguous 4*d-byte block, and goes to block
+// meta_base[r][h] + p of the min-max cache, not to the page's physical KV
+// slot: each head's bounds form one contiguous run in page order.
 #include "kvs_device.h"
 
 namespace kvs {
@@ -33,6 +35,8 @@ __global__ __launch_bounds__(256) void minmax_kernel(CacheView c) {
   const int gi = hs / c.Hp, slot = hs % c.Hp;
   const int phys = c.page_table[((int64_t)r * c.G + gi) * c.maxpg + p];
   if (phys < 0 || phys >= c.num_pages) return;
+  const int64_t meta = (int64_t)c.meta_base[r * c.Hkv + h] + p;
+  if (meta < 0 || meta >= c.num_meta) return;
   const int valid = min(P, n - p * P);
 
   const int rg = lane / COLS, col = lane % COLS;
@@ -67,7 +71,7 @@ __global__ __launch_bounds__(256) void minmax_kernel(CacheView c) {
   }
   if (rg == 0) {
     // channel-interleaved: (min, max) of channel ch at elements 2 ch, 2 ch + 1
-    uint16_t* mm = reinterpret_cast<uint16_t*>(c.minmax) + ((int64_t)phys * c.Hp + slot) * 2 * D;
+    uint16_t* mm = reinterpret_cast<uint16_t*>(c.minmax) + meta * 2 * D;
     uint4 a, b;
     a.x = pack2(lo[0], hi[0], DT());
     a.y = pack2(lo[1], hi[1], DT());

@@ -7,20 +7,33 @@
 // sign bits picks the right bound of both channels, and one pair-dot adds
 // the two products (equal values, one fewer product).
 //
-// One wave walks a chunk of 64 pages of one (request, head).  The chunk's
-// physical page ids are fetched first, one per lane.  A page of one head is
-// one contiguous 4*d-byte block, served by 8 lanes: load k of lane l reads
-// 16 bytes (4 channels, both bounds) at quad 8k + l % 8 of page l / 8, so
-// each load instruction reads one whole 128-byte line of each of 8 pages,
-// and a page's sum is 3 DPP levels over its 8 lanes.  Steps (8 pages each)
-// go in double-buffered rounds: the next round's loads are in flight while
-// the current one is scored.  The butterfly order is fixed: deterministic.
+// The work is a stream: every head's bounds are one contiguous run of
+// 4*d-byte blocks (block meta_base[r][h] + p), and the read is bound by HBM.
+// Heads differ widely in page count, so the grid is sized to what the chip
+// holds at once and the pages are dealt out evenly: each block first forms
+// the prefix sum of the heads' page counts in LDS; wave w of W then takes
+// flat pages [T*w/W, T*(w+1)/W) of the T in all heads, which it walks as one
+// segment per head it touches.  A segment loads its head's query rows once,
+// then streams rounds of pages: a page is served by 8 lanes, load k of lane
+// l reading 16 bytes (4 channels, both bounds) at quad 8k + l % 8 of page
+// l / 8, so each load instruction reads one whole 128-byte line of each of 8
+// neighbouring pages, and a page's sum is 3 DPP levels over its 8 lanes.
+// Rounds are double-buffered: the next round's loads are in flight while
+// the current one is scored.  Every load is unconditional (round indices and
+// pages are clamped into the segment, repeats hit the cache), which keeps
+// the compiler's wait counting exact.  The page table is read beside the
+// bounds only to give null pages -inf; pages past a head's end get -inf
+// from a final block-strided fill.  The butterfly order is fixed:
+// deterministic.
+#include <atomic>
+
 #include "kvs_device.h"
 
 namespace kvs {
 namespace {
 
-constexpr int kChunk = 64;   // pages per wave, one page id per lane
+constexpr int kThreads = 256;
+constexpr int kMaxDevices = 64;
 
 // Byte selector for v_perm_b32(b, a, sel) with a = (min_c, max_c) and
 // b = (min_c1, max_c1): low half from a (max if q_c >= 0), high half from b.
@@ -31,110 +44,190 @@ __device__ __forceinline__ uint32_t pick_selector(uint32_t q_pair) {
   return lo | (hi << 16);
 }
 
-template <int D, int GQ, typename DT>
-__global__ __launch_bounds__(256) void score_kernel(CacheView c, const uint16_t* __restrict__ q,
-                                                    float* __restrict__ scores) {
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ int page_count(const CacheView& c, int rh) {
   constexpr int P = 16;
+  return (clampi(c.seq_len[rh], 0, P * c.maxpg) + P - 1) / P;
+}
+
+// pre[i] = pages of heads (r, h) with r * Hkv + h < i, for i in [0, b * Hkv];
+// pre[b * Hkv] is the total.
+__device__ void page_prefix(const CacheView& c, int* pre, int* part) {
+  const int BH = c.b * c.Hkv;
+  const int tid = threadIdx.x;
+  const int per = (BH + kThreads - 1) / kThreads;
+  const int lo = min(BH, tid * per), hi = min(BH, lo + per);
+  int s = 0;
+  for (int i = lo; i < hi; ++i) s += page_count(c, i);
+  part[tid] = s;
+  __syncthreads();
+  if (tid < 64) {   // exclusive scan of the 256 partial sums, 4 per lane
+    int v[4], t = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[k] = part[4 * tid + k];
+      t += v[k];
+    }
+    int incl = t;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int n = __shfl_up(incl, off, 64);
+      if (tid >= off) incl += n;
+    }
+    int run = incl - t;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      part[4 * tid + k] = run;
+      run += v[k];
+    }
+  }
+  __syncthreads();
+  int run = part[tid];
+  for (int i = lo; i < hi; ++i) {
+    pre[i] = run;
+    run += page_count(c, i);
+  }
+  if (tid == kThreads - 1) pre[BH] = run;
+  __syncthreads();
+}
+
+template <int D, int GQ, typename DT>
+__global__ __launch_bounds__(kThreads) void score_kernel(CacheView c, const uint16_t* __restrict__ q,
+                                                         float* __restrict__ scores) {
   constexpr int LOADS = D / 32;           // 16-byte loads per lane per page
   constexpr int PPW = 8;                  // pages per step (8 lanes each)
-  constexpr int STEPS = kChunk / PPW;     // 8
   constexpr int UNROLL = 16 / LOADS;      // steps per round: 64 data registers
-  constexpr int ROUNDS = STEPS / UNROLL;
-  static_assert(STEPS % UNROLL == 0, "unroll");
+  constexpr int RP = PPW * UNROLL;        // pages per round
+  extern __shared__ int pre[];
+  __shared__ int part[kThreads];
+  page_prefix(c, pre, part);
+
+  const int BH = c.b * c.Hkv;
   const int lane = threadIdx.x & 63;
-  const int chunks = (c.maxpg + kChunk - 1) / kChunk;
-  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (wave >= (int64_t)c.b * c.Hkv * chunks) return;
-  const int chunk = (int)(wave % chunks);
-  const int rh = (int)(wave / chunks);
-  const int r = rh / c.Hkv, h = rh % c.Hkv;
-  const int n = clampi(c.seq_len[rh], 0, P * c.maxpg);
-  const int npg = (n + P - 1) / P;
-  const int hs = c.head_slot[h];
-  const bool head_ok = hs >= 0 && hs < c.Hkv;
-  const int gi = head_ok ? hs / c.Hp : 0, slot = head_ok ? hs % c.Hp : 0;
-  const int pbase = chunk * kChunk;
-  float* out = scores + (int64_t)rh * c.maxpg;
-
-  // Physical id of page pbase + lane (-1 if absent or out of range).
-  int my_phys = -1;
-  if (head_ok && pbase + lane < npg) {
-    my_phys = c.page_table[((int64_t)r * c.G + gi) * c.maxpg + pbase + lane];
-    if (my_phys >= c.num_pages) my_phys = -1;
-  }
-  if (pbase >= npg) {   // nothing to score: pad with -inf
-    if (pbase + lane < c.maxpg) out[pbase + lane] = -__builtin_inff();
-    return;
-  }
-
   const int pp = lane / 8, ql = lane % 8;   // page of the step, lane within the page
-  uint32_t qw[GQ][LOADS][2], sel[GQ][LOADS][2];
-#pragma unroll
-  for (int g = 0; g < GQ; ++g) {
-    const uint16_t* qrow = q + ((int64_t)r * c.Hq + h * GQ + g) * D;
-#pragma unroll
-    for (int k = 0; k < LOADS; ++k) {
-      const uint2 v = *reinterpret_cast<const uint2*>(qrow + 4 * (8 * k + ql));
-      qw[g][k][0] = v.x;
-      qw[g][k][1] = v.y;
-      sel[g][k][0] = pick_selector(v.x);
-      sel[g][k][1] = pick_selector(v.y);
+  const int64_t W = (int64_t)gridDim.x * (kThreads / 64);
+  const int64_t w = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int64_t T = uni(pre[BH]);
+  int t0 = (int)(T * w / W);
+  const int t1 = (int)(T * (w + 1) / W);
+  // head holding flat page t0: the largest hh with pre[hh] <= t0 (non-empty)
+  int hh = 0;
+  {
+    int lo = 0, hi = BH;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) / 2;
+      if (uni(pre[mid]) <= t0) lo = mid; else hi = mid - 1;
     }
+    hh = lo;
   }
-  const uint16_t* mm = reinterpret_cast<const uint16_t*>(c.minmax) + slot * 2 * D + 8 * ql;
-  const int64_t page_stride = (int64_t)c.Hp * 2 * D;
+  const int64_t last = c.num_meta - 1;
+  const uint16_t* mmb = reinterpret_cast<const uint16_t*>(c.minmax) + 8 * ql;
 
-  // Loads are unconditional (a missing page reads page 0 and is discarded),
-  // which keeps the compiler's wait counting exact across the pipeline.
-  uint4 mmv[2][UNROLL][LOADS];
-  int live[2][UNROLL];
-  auto issue = [&](int s0, uint4 (&dst)[UNROLL][LOADS], int (&ok)[UNROLL]) {
+  while (t0 < t1) {
+    const int rh = hh;
+    const int base = uni(pre[rh]);
+    const int seg_end = min(t1, uni(pre[rh + 1]));
+    const int p0 = t0 - base, p1 = seg_end - base;   // pages [p0, p1) of head rh
+    const int r = rh / c.Hkv, h = rh - r * c.Hkv;
+    const int hs = c.head_slot[h];
+    const bool head_ok = hs >= 0 && hs < c.Hkv;
+    const int gi = head_ok ? hs / c.Hp : 0;
+    const int32_t* ptrow = c.page_table + ((int64_t)r * c.G + gi) * c.maxpg;
+    const int64_t mb = c.meta_base[rh];
+    float* out = scores + (int64_t)rh * c.maxpg;
+
+    uint32_t qw[GQ][LOADS][2], sel[GQ][LOADS][2];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int phys = __shfl(my_phys, (s0 + u) * PPW + pp, 64);
-      ok[u] = phys >= 0;
-      const uint16_t* base = mm + (phys >= 0 ? phys : 0) * page_stride;
+    for (int g = 0; g < GQ; ++g) {
+      const uint16_t* qrow = q + ((int64_t)r * c.Hq + h * GQ + g) * D;
 #pragma unroll
-      for (int k = 0; k < LOADS; ++k) dst[u][k] = ld16(base + 64 * k);
-    }
-  };
-  auto score = [&](int s0, const uint4 (&src)[UNROLL][LOADS], const int (&ok)[UNROLL]) {
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      float best = -__builtin_inff();
-#pragma unroll
-      for (int g = 0; g < GQ; ++g) {
-        float acc = 0.f;
-#pragma unroll
-        for (int k = 0; k < LOADS; ++k) {
-          const uint4 w = src[u][k];
-          acc = dot2(qw[g][k][0], __builtin_amdgcn_perm(w.y, w.x, sel[g][k][0]), acc, DT());
-          acc = dot2(qw[g][k][1], __builtin_amdgcn_perm(w.w, w.z, sel[g][k][1]), acc, DT());
-        }
-        best = fmaxf(best, group_sum<8>(acc));
+      for (int k = 0; k < LOADS; ++k) {
+        const uint2 v = *reinterpret_cast<const uint2*>(qrow + 4 * (8 * k + ql));
+        qw[g][k][0] = v.x;
+        qw[g][k][1] = v.y;
+        sel[g][k][0] = pick_selector(v.x);
+        sel[g][k][1] = pick_selector(v.y);
       }
-      const int p = pbase + (s0 + u) * PPW + pp;
-      if (ql == 0 && p < c.maxpg) out[p] = ok[u] ? best : -__builtin_inff();
     }
-  };
-  // two rounds per iteration so both buffers are named statically
-  issue(0, mmv[0], live[0]);
-  for (int rd = 0; rd < ROUNDS; rd += 2) {
-    if (rd + 1 < ROUNDS) issue((rd + 1) * UNROLL, mmv[1], live[1]);
-    score(rd * UNROLL, mmv[0], live[0]);
-    if (rd + 1 < ROUNDS) {
-      if (rd + 2 < ROUNDS) issue((rd + 2) * UNROLL, mmv[0], live[0]);
-      score((rd + 1) * UNROLL, mmv[1], live[1]);
+
+    uint4 mmv[2][UNROLL][LOADS];
+    int ptv[2][UNROLL];
+    auto issue = [&](int rd, uint4 (&dst)[UNROLL][LOADS], int (&pt)[UNROLL]) {
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        const int p = min(p0 + rd * RP + u * PPW + pp, p1 - 1);
+        int64_t m = mb + p;
+        m = m < 0 ? 0 : (m > last ? last : m);
+        const uint16_t* bp = mmb + m * (2 * D);
+#pragma unroll
+        for (int k = 0; k < LOADS; ++k) dst[u][k] = ld16(bp + 64 * k);
+        pt[u] = ptrow[p];
+      }
+    };
+    auto score = [&](int rd, const uint4 (&src)[UNROLL][LOADS], const int (&pt)[UNROLL]) {
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) {
+        float best = -__builtin_inff();
+#pragma unroll
+        for (int g = 0; g < GQ; ++g) {
+          float acc = 0.f;
+#pragma unroll
+          for (int k = 0; k < LOADS; ++k) {
+            const uint4 v = src[u][k];
+            acc = dot2(qw[g][k][0], __builtin_amdgcn_perm(v.y, v.x, sel[g][k][0]), acc, DT());
+            acc = dot2(qw[g][k][1], __builtin_amdgcn_perm(v.w, v.z, sel[g][k][1]), acc, DT());
+          }
+          best = fmaxf(best, group_sum<8>(acc));
+        }
+        const int p = p0 + rd * RP + u * PPW + pp;
+        const int64_t m = mb + p;
+        const bool ok = head_ok && pt[u] >= 0 && pt[u] < c.num_pages && m >= 0 && m <= last;
+        if (ql == 0 && p < p1) out[p] = ok ? best : -__builtin_inff();
+      }
+    };
+    const int rounds = (p1 - p0 + RP - 1) / RP;
+    issue(0, mmv[0], ptv[0]);
+    for (int rd = 0; rd < rounds; rd += 2) {
+      issue(min(rd + 1, rounds - 1), mmv[1], ptv[1]);
+      score(rd, mmv[0], ptv[0]);
+      issue(min(rd + 2, rounds - 1), mmv[0], ptv[0]);
+      if (rd + 1 < rounds) score(rd + 1, mmv[1], ptv[1]);
     }
+
+    t0 = seg_end;
+    while (hh < BH && uni(pre[hh + 1]) <= t0) ++hh;
+  }
+
+  // -inf past each head's pages
+  for (int rh = blockIdx.x; rh < BH; rh += gridDim.x) {
+    const int npg = pre[rh + 1] - pre[rh];
+    float* out = scores + (int64_t)rh * c.maxpg;
+    for (int p = npg + (int)threadIdx.x; p < c.maxpg; p += kThreads) out[p] = -__builtin_inff();
   }
 }
 
 template <int D, int GQ, typename DT>
 hipError_t launch_v(const CacheView& c, const void* q, float* scores, hipStream_t s) {
-  const int chunks = (c.maxpg + kChunk - 1) / kChunk;
-  const int64_t waves = (int64_t)c.b * c.Hkv * chunks;
-  const int64_t blocks = (waves + 3) / 4;
-  hipLaunchKernelGGL((score_kernel<D, GQ, DT>), dim3((unsigned)blocks), dim3(256), 0, s, c,
+  // One resident wave per slot: compute units x resident blocks per unit,
+  // found once per device.
+  static std::atomic<int> grid_of[kMaxDevices];
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  int grid = grid_of[dev].load(std::memory_order_relaxed);
+  if (grid == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev))
+      return e;
+    if (hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(score_kernel<D, GQ, DT>), kThreads, 0))
+      return e;
+    grid = max(1, cus * max(1, per_cu));
+    grid_of[dev].store(grid, std::memory_order_relaxed);
+  }
+  const size_t lds = (size_t)(c.b * c.Hkv + 1) * sizeof(int);
+  hipLaunchKernelGGL((score_kernel<D, GQ, DT>), dim3((unsigned)grid), dim3(kThreads), lds, s, c,
                      static_cast<const uint16_t*>(q), scores);
   return hipGetLastError();
 }

@@ -40,13 +40,14 @@ class PagedKV(ctypes.Structure):
     _fields_ = [
         ("kv", ctypes.c_void_p),
         ("minmax", ctypes.c_void_p),
+        ("meta_base", ctypes.c_void_p),
         ("page_table", ctypes.c_void_p),
         ("seq_len", ctypes.c_void_p),
         ("head_slot", ctypes.c_void_p),
         ("b", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
         ("Hp", ctypes.c_int32), ("d", ctypes.c_int32), ("P", ctypes.c_int32),
         ("max_group_pages", ctypes.c_int32), ("num_pages", ctypes.c_int32),
-        ("dtype", ctypes.c_int32),
+        ("num_meta", ctypes.c_int32), ("dtype", ctypes.c_int32),
     ]
 
 
@@ -128,7 +129,8 @@ def _need(t: torch.Tensor, name: str, shape, dtype, device=None) -> None:
 class Cache:
     """One layer's paged KV as device tensors (the fields of kvs_paged_kv)."""
     kv: torch.Tensor            # [num_pages][Hp][2][P][d]
-    minmax: torch.Tensor        # [num_pages][Hp][d][2]
+    minmax: torch.Tensor        # [num_meta][d][2], per-head runs in page order
+    meta_base: torch.Tensor     # int32 [b][Hkv]: first min-max block of each head
     page_table: torch.Tensor    # int32 [b][G][max_group_pages]
     seq_len: torch.Tensor       # int32 [b][Hkv]
     head_slot: torch.Tensor     # int32 [Hkv]
@@ -140,13 +142,16 @@ class Cache:
         Hkv = self.seq_len.shape[1]
         dev = self.kv.device
         _need(self.kv, "kv", (num_pages, Hp, 2, P, d), self.kv.dtype, dev)
-        _need(self.minmax, "minmax", (num_pages, Hp, d, 2), self.kv.dtype, dev)
+        num_meta = self.minmax.shape[0]
+        _need(self.minmax, "minmax", (num_meta, d, 2), self.kv.dtype, dev)
+        _need(self.meta_base, "meta_base", (b, Hkv), torch.int32, dev)
         _need(self.page_table, "page_table", (b, Hkv // Hp, maxpg), torch.int32, dev)
         _need(self.seq_len, "seq_len", (b, Hkv), torch.int32, dev)
         _need(self.head_slot, "head_slot", (Hkv,), torch.int32, dev)
-        return PagedKV(self.kv.data_ptr(), self.minmax.data_ptr(), self.page_table.data_ptr(),
-                       self.seq_len.data_ptr(), self.head_slot.data_ptr(), b, self.Hq, Hkv, Hp,
-                       d, P, maxpg, num_pages, dtype_code(self.kv.dtype))
+        return PagedKV(self.kv.data_ptr(), self.minmax.data_ptr(), self.meta_base.data_ptr(),
+                       self.page_table.data_ptr(), self.seq_len.data_ptr(),
+                       self.head_slot.data_ptr(), b, self.Hq, Hkv, Hp, d, P, maxpg, num_pages,
+                       num_meta, dtype_code(self.kv.dtype))
 
 
 def kvs_build_minmax(cache: Cache, stream=None) -> None:

@@ -9,6 +9,12 @@ handed out in a seeded shuffled order so that the kernels' table walks are
 exercised, not bypassed by a contiguous layout.  Unused pool slots are
 filled with NaN so that any read of an invalid token shows up in the output.
 
+The min-max cache (FlexiCache summary, Key observations, assumption 2: page
+bounds kept on the GPU apart from the KV pages) is ragged per head: each
+(request, head) owns a contiguous run of ceil(n/P) blocks starting at
+meta_base[r][h], so scoring streams a head's bounds in page order however
+its KV pages are scattered.
+
 Layers whose data share a bank (workload layers l and l + data_layers) share
 one physical pool: each (request, group) gets as many pages as the largest
 of those layers needs, and every layer has its own page table (a prefix of
@@ -33,6 +39,7 @@ __all__ = ["build_caches", "RaggedLayout"]
 class RaggedLayout:
     """Host copy of one layer's tables."""
     page_table: np.ndarray   # [b][G][maxpg] int32, -1 null
+    meta_base: np.ndarray    # [b][Hkv] int32, first min-max block of each head
     seq_len: np.ndarray      # [b][Hkv] int32
     head_slot: np.ndarray    # [Hkv] int32
     pool: int                # physical pool index
@@ -108,15 +115,17 @@ def build_caches(wl: Workload, head_slot: np.ndarray, device="cuda", poison: boo
                     k = int(need[l, r, i])
                     pt[r, i, :k] = pages(r, i)[:k]
             seq = wl.n[:, l, :].astype(np.int32)
-            mm = torch.empty((total, Hp, d, 2), dtype=dt, device=device)
+            runs = (-(-wl.n[:, l, :] // P)).reshape(-1)
+            mb = np.concatenate([[0], np.cumsum(runs)[:-1]]).astype(np.int32).reshape(c.b, c.Hkv)
+            mm = torch.empty((max(1, int(runs.sum())), d, 2), dtype=dt, device=device)
             if poison:
                 _nan_fill(mm)
-            caches[l] = Cache(kv=kv, minmax=mm,
+            caches[l] = Cache(kv=kv, minmax=mm, meta_base=torch.from_numpy(mb).to(device),
                               page_table=torch.from_numpy(pt).to(device),
                               seq_len=torch.from_numpy(np.ascontiguousarray(seq)).to(device),
                               head_slot=torch.from_numpy(hs[l].astype(np.int32)).to(device),
                               Hq=c.Hq)
-            layouts[l] = RaggedLayout(page_table=pt, seq_len=seq,
+            layouts[l] = RaggedLayout(page_table=pt, meta_base=mb, seq_len=seq,
                                       head_slot=hs[l].astype(np.int32), pool=lam)
     return caches, layouts
 

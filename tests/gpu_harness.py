@@ -98,8 +98,8 @@ def check_layer(step: DecodeStep, l: int, q: torch.Tensor, requests: Sequence[in
             assert K64.shape[0] == n
             lo, hi = O.page_minmax(K64, c.P)
             if check_minmax or c.topk:
-                ids = torch.as_tensor(lay.page_table[r, gi, :npg].astype(np.int64), device=dev)
-                g_mm = mm[ids, j].double().cpu().numpy()         # [npg][d][2]
+                m0 = int(lay.meta_base[r, h])
+                g_mm = mm[m0:m0 + npg].double().cpu().numpy()     # [npg][d][2]
                 if check_minmax:
                     assert np.array_equal(g_mm[:, :, 0], lo), f"kmin r={r} l={l} h={h}"
                     assert np.array_equal(g_mm[:, :, 1], hi), f"kmax r={r} l={l} h={h}"

@@ -10,7 +10,8 @@ import pytest
 import torch
 
 import oracle as O
-from gpu_harness import Stats, assert_output_bar, check_layer, require_gpu, say
+from gpu_harness import (OUT_MAX_ABS, SCORE_TOL, Stats, assert_output_bar, check_layer,
+                         require_gpu, say)
 from non_uniform_sparse_amd import kvs
 from non_uniform_sparse_amd.pipeline import DecodeStep
 from non_uniform_sparse_amd.workloads import make_workload
@@ -130,6 +131,73 @@ def test_edge_cases(Hp, d, Hq, dtype, n_list, topk):
         st = Stats()
         check_layer(step, 0, step.queries()[0], range(c.b), st)
         assert_output_bar(st, f"edge T={T}")
+
+
+@pytest.mark.parametrize("topk", [None, 2])
+def test_null_page_entries(topk):
+    """Null (-1) page-table entries: the min-max builder leaves their blocks
+    untouched, scoring gives them -inf, and decode leaves their tokens out.
+    Page 0 of every group stays valid, so every head keeps some tokens."""
+    require_gpu()
+    wl = make_workload("llama8b_ragged", b=2, N=400, Hq=32, d=128, dtype="f16", Hp=4, topk=topk)
+    wl.n[0, 0, :] = [40, 1, 16, 300, 64, 65, 17, 2]
+    wl.n[1, 0, :] = [100, 33, 250, 49, 16, 80, 5, 129]
+    say(f"[case] null pages topk={topk}")
+    c = wl.cfg
+    step = DecodeStep(wl, device="cuda")
+    cache, lay = step.caches[0], step.layouts[0]
+    nulls = {(0, 0): [1], (0, 1): [2, 5], (1, 0): [3], (1, 1): [1, 7]}
+    pt = lay.page_table.copy()
+    for (r, i), ps in nulls.items():
+        pt[r, i, [p for p in ps if p < pt.shape[2]]] = -1
+    cache.page_table.copy_(torch.from_numpy(pt))
+    cache.minmax.view(torch.int16).fill_(0x7E00)
+    kvs.kvs_build_minmax(cache)
+    q = step.queries()[0]
+    if topk:
+        step.select(0, q)
+    out = step.attend(0, q).cpu().numpy().astype(np.float64)
+    mm = cache.minmax.double().cpu().numpy()
+    q64 = q.double().cpu().numpy()
+    buf = step.bufs[0]
+    hit = 0
+    for r in range(c.b):
+        for h in range(c.Hkv):
+            pos = int(step.head_slot[0, h])
+            gi, j = pos // c.Hp, pos % c.Hp
+            n = int(wl.n[r, 0, h])
+            npg = -(-n // c.P)
+            null = sorted(p for p in nulls.get((r, gi), []) if p < npg)
+            hit += len(null)
+            K64, V64 = wl.head_kv(r, 0, h, pos, device="cuda")
+            K64, V64 = K64.double().cpu().numpy(), V64.double().cpu().numpy()
+            lo, hi = O.page_minmax(K64, c.P)
+            m0 = int(lay.meta_base[r, h])
+            for p in range(npg):
+                blk = mm[m0 + p]
+                if p in null:
+                    assert np.all(np.isnan(blk)), f"null page written r={r} h={h} p={p}"
+                else:
+                    assert np.array_equal(blk[:, 0], lo[p]) and np.array_equal(blk[:, 1], hi[p])
+            qg = q64[r, h * c.Gq:(h + 1) * c.Gq]
+            if topk:
+                s = buf.scores[r, h, :npg].cpu().numpy()
+                assert np.all(np.isneginf(s[null]))
+                keep = [p for p in range(npg) if p not in null]
+                want = O.page_scores(qg, lo[keep], hi[keep])
+                A = np.max(np.abs(qg[:, None, :] * lo[keep][None]).sum(-1) +
+                           np.abs(qg[:, None, :] * hi[keep][None]).sum(-1), axis=0)
+                assert np.all(np.abs(s[keep] - want) <= SCORE_TOL * A)
+                cnt = int(buf.sel_count[r, h])
+                got = buf.sel[r, h, :cnt].cpu().numpy()
+                assert np.array_equal(got, O.topk_pages(s, topk))
+                pages = np.array([p for p in got if p not in null], dtype=np.int64)
+            else:
+                pages = np.array([p for p in range(npg) if p not in null], dtype=np.int64)
+            ref = O.decode_head(qg, K64, V64, pages, c.P, step.scale)
+            err = float(np.abs(out[r, h * c.Gq:(h + 1) * c.Gq] - ref).max())
+            assert err <= OUT_MAX_ABS, f"r={r} h={h} err={err}"
+    assert hit >= 4, "the case should null some pages of real heads"
 
 
 def test_deterministic():

@@ -129,9 +129,9 @@ class _FakeCache:
     """A descriptor with fake (never dereferenced) device pointers."""
 
     def __init__(self, **kw):
-        f = dict(kv=0x10000, minmax=0x20000, page_table=0x30000, seq_len=0x40000,
-                 head_slot=0x50000, b=1, Hq=32, Hkv=8, Hp=4, d=128, P=16,
-                 max_group_pages=4, num_pages=8, dtype=kvs.KVS_F16)
+        f = dict(kv=0x10000, minmax=0x20000, meta_base=0x28000, page_table=0x30000,
+                 seq_len=0x40000, head_slot=0x50000, b=1, Hq=32, Hkv=8, Hp=4, d=128, P=16,
+                 max_group_pages=4, num_pages=8, num_meta=8, dtype=kvs.KVS_F16)
         f.update(kw)
         self.s = kvs.PagedKV(**f)
 
@@ -146,6 +146,8 @@ class _FakeCache:
     (dict(dtype=7), kvs.KVS_EUNSUPPORTED),
     (dict(Hq=24), kvs.KVS_EUNSUPPORTED),      # query group of 3
     (dict(b=0), kvs.KVS_EINVAL),
+    (dict(meta_base=0), kvs.KVS_EINVAL),
+    (dict(num_meta=0), kvs.KVS_EINVAL),
 ])
 def test_validation_before_launch(kw, code):
     L = _lib()
