@@ -99,11 +99,13 @@ def cpu_baseline(wl, step, budget_s: float = 12.0) -> dict:
     except Exception:  # pragma: no cover
         cores = 1
     c = wl.cfg
-    q = [wl.q(l, device=step.device).double().cpu().numpy() for l in range(min(c.L, 4))]
+    q = {}
     scale = 1.0 / math.sqrt(c.d)
     done_bytes, spent, heads = 0, 0.0, 0
-    order = [(r, l, h) for l in range(min(c.L, 4)) for r in range(c.b) for h in range(c.Hkv)]
+    order = [(r, l, h) for l in range(c.L) for r in range(c.b) for h in range(c.Hkv)]
     for r, l, h in order:
+        if l not in q:
+            q[l] = wl.q(l, device=step.device).double().cpu().numpy()
         pos = int(step.head_slot[l, h])
         K, V = wl.head_kv(r, l, h, pos, device=step.device)
         K, V = K.double().cpu().numpy(), V.double().cpu().numpy()
@@ -174,6 +176,19 @@ def skew_report(configs, launches: int = 20) -> dict:
     return out
 
 
+def sleep_rate(stream) -> float:
+    """Spin cycles per millisecond of torch's GPU sleep kernel, measured."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 1 << 20
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(n)
+        a.record(stream)
+        torch.cuda._sleep(n)
+        b.record(stream)
+    b.synchronize()
+    return n / max(a.elapsed_time(b), 1e-3)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -233,17 +248,24 @@ def main() -> int:
     ab = [algorithmic_bytes(step, l) for l in range(c.L)]
     kv_bytes = sum(a["kv"] for a in ab)
     path_bytes = sum(a["kv"] + a["meta"] + a["small"] for a in ab)
-    # Working sets that could sit in L2 / MALL (256 MB) are flushed before each step.
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if path_bytes < 8e9 else None
+    # Working sets that could sit in L2 / MALL (256 MB) are evicted before
+    # each step by reading 1 GB (a read leaves no dirty lines behind to be
+    # written back inside the timed step).
+    flush = torch.ones(1 << 27, dtype=torch.int64, device=dev) if path_bytes < 8e9 else None
     ev = lambda: torch.cuda.Event(enable_timing=True)
+    cycles_per_ms = sleep_rate(stream)
 
     # Pass 1 (eager, per-kernel HIP events on the launch stream): kernel
-    # durations for the roofline figures.
+    # durations for the roofline figures.  Each step is queued behind a GPU
+    # spin long enough for the host to enqueue the whole step, so the
+    # kernels run back to back and the events time kernels, not host
+    # launch latency.
     kern = {"score": [], "topk": [], "decode_attn": []}
     for _ in range(args.steps):
-        if flush is not None:
-            with torch.cuda.stream(stream):
-                flush.zero_()
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(int(cycles_per_ms * (2.0 + 0.4 * c.L)))
+            if flush is not None:
+                flush.sum()
         marks = []
         for l in range(c.L):
             q = qs[l]
@@ -273,22 +295,23 @@ def main() -> int:
     for _ in range(args.warmup):
         graph.replay()
     torch.cuda.synchronize()
-    step_ms = []
+    marks = []
     wall0 = time.perf_counter()
     for _ in range(args.steps):
         if flush is not None:
-            flush.zero_()
+            flush.sum()
         s0, s1 = ev(), ev()
         s0.record(cur)
         graph.replay()
         s1.record(cur)
-        if flush is not None:
-            s1.synchronize()
-            step_ms.append(s0.elapsed_time(s1))
+        marks.append((s0, s1))
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - wall0) * 1e3
 
-    ms = statistics.mean(step_ms) if flush is not None else wall_ms / args.steps
+    # With flushes the steps are timed one by one (the flush is not step
+    # work); without, the wall clock over the K back-to-back replays.
+    ms = (statistics.mean(a.elapsed_time(b_) for a, b_ in marks) if flush is not None
+          else wall_ms / args.steps)
     dec_ms = statistics.mean(kern["decode_attn"])
     dec_bytes = statistics.mean(a["decode_launch"] for a in ab)
     achieved = dec_bytes / (dec_ms * 1e-3) / 1e9

@@ -105,8 +105,9 @@ def _counter(path, counter, pattern):
 
 def write_traffic(workload, fetch, write, copy_fetch, copy_write, out, cmd) -> dict:
     kib = 1024.0
-    cf = _counter(copy_fetch, "FETCH_SIZE", r"copy|elementwise") * kib
-    cw = _counter(copy_write, "WRITE_SIZE", r"copy|elementwise") * kib
+    # only the copy kernel: the probe's source fill writes 1 GiB too
+    cf = _counter(copy_fetch, "FETCH_SIZE", r"copy") * kib
+    cw = _counter(copy_write, "WRITE_SIZE", r"copy") * kib
     fs, ws = COPY_BYTES / cf, COPY_BYTES / cw
     f = _counter(fetch, "FETCH_SIZE", r"decode_kernel|combine_kernel") * kib * fs
     w = _counter(write, "WRITE_SIZE", r"decode_kernel|combine_kernel") * kib * ws
