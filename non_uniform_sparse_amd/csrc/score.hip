@@ -52,14 +52,28 @@ __device__ __forceinline__ int page_count(const CacheView& c, int rh) {
 }
 
 // pre[i] = pages of heads (r, h) with r * Hkv + h < i, for i in [0, b * Hkv];
-// pre[b * Hkv] is the total.
+// pre[b * Hkv] is the total.  The page counts are first loaded into pre[]
+// with coalesced loads, up to 8 in flight per thread, then summed per
+// contiguous chunk, scanned, and overwritten in place by the prefix.
 __device__ void page_prefix(const CacheView& c, int* pre, int* part) {
   const int BH = c.b * c.Hkv;
   const int tid = threadIdx.x;
+  constexpr int CH = 8;
+  for (int base = 0; base < BH; base += kThreads * CH) {
+    int v[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) v[j] = page_count(c, min(base + j * kThreads + tid, BH - 1));
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int i = base + j * kThreads + tid;
+      if (i < BH) pre[i] = v[j];
+    }
+  }
+  __syncthreads();
   const int per = (BH + kThreads - 1) / kThreads;
   const int lo = min(BH, tid * per), hi = min(BH, lo + per);
   int s = 0;
-  for (int i = lo; i < hi; ++i) s += page_count(c, i);
+  for (int i = lo; i < hi; ++i) s += pre[i];
   part[tid] = s;
   __syncthreads();
   if (tid < 64) {   // exclusive scan of the 256 partial sums, 4 per lane
@@ -85,8 +99,9 @@ __device__ void page_prefix(const CacheView& c, int* pre, int* part) {
   __syncthreads();
   int run = part[tid];
   for (int i = lo; i < hi; ++i) {
+    const int n = pre[i];
     pre[i] = run;
-    run += page_count(c, i);
+    run += n;
   }
   if (tid == kThreads - 1) pre[BH] = run;
   __syncthreads();

@@ -8,9 +8,12 @@
 // lane), a suffix scan over its lanes gives the count above each lane's bins
 // and the one lane whose bins straddle the K-th key publishes the digit.
 // Pages with key > tau are kept, and among pages with key == tau the lowest
-// page indices fill the remaining places; ballots and per-wave counts over
-// 256-page windows rank the ties and place the kept pages in ascending page
-// order.  Integer work only, so the result is deterministic.
+// page indices fill the remaining places.  To place them, each thread owns
+// one contiguous run of pages and counts its keys above and equal to tau;
+// one block-wide exclusive scan of the two counts (packed in one int) gives
+// each thread its first output position and the ties taken before it, and
+// the thread writes its kept pages in page order.  Integer work only, so the
+// result is deterministic.
 #include "kvs_device.h"
 
 namespace kvs {
@@ -23,14 +26,26 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Number of set bits of m in lanes below this one.
-__device__ __forceinline__ int rank_below(uint64_t m) {
-  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
-
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+
+// Block-wide exclusive prefix sum of one int per thread, in thread order.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* red) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += t;
+  }
+  if (lane == 63) red[wid] = incl;
+  __syncthreads();
+  int before = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) before += w < wid ? red[w] : 0;
+  __syncthreads();
+  return before + incl - v;
+}
 
 // Block-wide min and max of one int per thread (every thread gets both).
 __device__ __forceinline__ void block_minmax(int lo, int hi, int* red, int* out_lo, int* out_hi) {
@@ -70,7 +85,19 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   const float* row = scores + (int64_t)rh * max_pages;
   int32_t* out = sel + (int64_t)rh * K;
 
-  for (int p = tid; p < npg; p += kThreads) keys[p] = order_key(row[p]);
+  // All of a thread's loads are issued before the first store, so a long
+  // row costs one memory round trip per 4096 pages, not one per 256.
+  constexpr int CH = 16;
+  for (int base = 0; base < npg; base += kThreads * CH) {
+    float v[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) v[j] = row[min(base + j * kThreads + tid, npg - 1)];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int p = base + j * kThreads + tid;
+      if (p < npg) keys[p] = order_key(v[j]);
+    }
+  }
   __syncthreads();
 
   uint32_t prefix = 0, mask = 0;
@@ -139,36 +166,31 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   const uint32_t tau = prefix;
   const int ties = need;
 
-  // Windows of 256 pages in page order: rank ties, then place kept pages.
-  int eq_before = 0, pos_before = 0;
-  for (int base = 0; base < npg; base += kThreads) {
-    const int p = base + tid;
-    const uint32_t k = p < npg ? keys[p] : 0u;
-    const bool eq = p < npg && k == tau;
-    const uint64_t eqm = __ballot(eq);
-    if (lane == 0) red[wid] = __popcll(eqm);
-    __syncthreads();
-    int eq_w = eq_before, eq_all = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      eq_w += w < wid ? red[w] : 0;
-      eq_all += red[w];
+  // Thread tid owns pages [p_lo, p_hi): count keys above and equal to tau
+  // (each count < 2^14 since max_pages <= 8192), scan, then place.
+  if (keep > 0) {
+    const int per = (npg + kThreads - 1) / kThreads;
+    const int p_lo = min(npg, tid * per), p_hi = min(npg, p_lo + per);
+    int n_gt = 0, n_eq = 0;
+    for (int p = p_lo; p < p_hi; ++p) {
+      const uint32_t k = keys[p];
+      n_gt += k > tau;
+      n_eq += k == tau;
     }
-    const bool take = keep > 0 && p < npg && (k > tau || (eq && eq_w + rank_below(eqm) < ties));
-    const uint64_t tm = __ballot(take);
-    if (lane == 0) red[kWaves + wid] = __popcll(tm);
-    __syncthreads();
-    int pos = pos_before, t_all = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      pos += w < wid ? red[kWaves + w] : 0;
-      t_all += red[kWaves + w];
+    const int before = block_exclusive_scan((n_gt << 16) | n_eq, red);
+    const int gt_before = before >> 16, eq_before = before & 0xffff;
+    int pos = gt_before + min(eq_before, ties);
+    int eq_seen = eq_before;
+    for (int p = p_lo; p < p_hi; ++p) {
+      const uint32_t k = keys[p];
+      const bool eq = k == tau;
+      const bool take = k > tau || (eq && eq_seen < ties);
+      eq_seen += eq;
+      if (take) {
+        if (pos < keep) out[pos] = p;
+        ++pos;
+      }
     }
-    pos += rank_below(tm);
-    if (take && pos < keep) out[pos] = p;
-    eq_before += eq_all;
-    pos_before += t_all;
-    __syncthreads();
   }
   for (int k = keep + tid; k < K; k += kThreads) out[k] = -1;
   if (tid == 0) sel_count[rh] = keep;

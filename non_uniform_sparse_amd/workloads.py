@@ -76,7 +76,7 @@ class Config:
 
     @property
     def nbanks(self) -> int:
-        return self.data_layers or self.L
+        return min(self.data_layers, self.L) if self.data_layers else self.L
 
 
 CONFIGS: Dict[str, Config] = {
