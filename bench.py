@@ -195,6 +195,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(CONFIGS))
+    ap.add_argument("--microbatches", type=int, default=3,
+                    help="request micro-batches, each on a stream of its own in the step graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--skew", nargs="*", default=None, metavar="CONFIG",
@@ -234,7 +236,7 @@ def main() -> int:
     t0 = time.time()
     wl = make_workload(args.config)
     c = wl.cfg
-    step = DecodeStep(wl, device=dev)
+    step = DecodeStep(wl, device=dev, microbatches=args.microbatches)
     qs = step.queries()
     torch.cuda.synchronize()
     log(f"[bench] {c.name}: set-up {time.time() - t0:.1f} s, W={step.W}, T={step.T}, "
@@ -288,8 +290,9 @@ def main() -> int:
         for k, a, b_ in marks:
             kern[k].append(a.elapsed_time(b_))
 
-    # Pass 2 (headline): the whole step captured once as a HIP graph and
-    # replayed; K steps timed between two synchronisations.
+    # Pass 2 (headline): the whole step captured once as a HIP graph (the
+    # request micro-batches on streams of their own) and replayed; K steps
+    # timed between two synchronisations.
     graph = step.capture(qs)
     cur = torch.cuda.current_stream()
     for _ in range(args.warmup):
@@ -340,6 +343,7 @@ def main() -> int:
             "kv_bytes_per_step": kv_bytes, "path_bytes_per_step": path_bytes,
             "cache_flush_between_steps": flush is not None,
             "step_launch": "hip_graph",
+            "microbatches": len(step.parts),
         },
         "kernels_ms_avg": {k: round(statistics.mean(v), 5) for k, v in kern.items() if v},
         "roofline": {

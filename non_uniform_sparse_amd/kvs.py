@@ -136,6 +136,13 @@ class Cache:
     head_slot: torch.Tensor     # int32 [Hkv]
     Hq: int
 
+    def rows(self, r0: int, r1: int) -> "Cache":
+        """The requests [r0, r1) as a cache of their own: views of the
+        per-request tables over the same pool and min-max cache."""
+        return Cache(kv=self.kv, minmax=self.minmax, meta_base=self.meta_base[r0:r1],
+                     page_table=self.page_table[r0:r1], seq_len=self.seq_len[r0:r1],
+                     head_slot=self.head_slot, Hq=self.Hq)
+
     def struct(self) -> PagedKV:
         num_pages, Hp, two, P, d = self.kv.shape
         b, G, maxpg = self.page_table.shape

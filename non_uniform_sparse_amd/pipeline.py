@@ -3,8 +3,15 @@
 Set-up (once): cluster heads by budget, build the ragged caches and their
 min-max metadata, plan the static split map, allocate the step's buffers.
 Step: for each layer, [score pages -> top-K pages ->] split-K decode +
-combine, all launched on one stream with no host synchronisation; the grid
-of every launch comes from the static split map, never from the data.
+combine, all launched with no host synchronisation; the grid of every
+launch comes from the static split map, never from the data.
+
+Micro-batches.  Requests are independent, so the batch can be cut into
+parts whose layer chains run on streams of their own, captured as one
+graph (fork, one chain per stream, join).  One part's latency-bound phases
+(top-K, kernel boundaries, the ramp and tail of each kernel) then overlap
+another part's HBM-bound ones.  Every request gets the same split row S[l]
+either way, so its result is the same bit for bit.
 """
 
 from __future__ import annotations
@@ -52,7 +59,7 @@ class LayerBuffers:
 class DecodeStep:
     def __init__(self, wl: Workload, device="cuda", T: Optional[int] = None,
                  head_slot: Optional[np.ndarray] = None, S: Optional[np.ndarray] = None,
-                 poison: bool = True):
+                 poison: bool = True, microbatches: int = 1):
         c = wl.cfg
         self.wl, self.cfg, self.device = wl, c, device
         if head_slot is None:
@@ -88,6 +95,12 @@ class DecodeStep:
                 scores = sel = cnt = None
             out = torch.empty((c.b, c.Hq, c.d), dtype=torch.float32, device=device)
             self.bufs.append(LayerBuffers(scores, sel, cnt, out))
+        mb = max(1, min(int(microbatches), c.b))
+        self.parts = [(c.b * k // mb, c.b * (k + 1) // mb) for k in range(mb)]
+        self.part_ws = [
+            torch.empty(max(kvs.kvs_decode_workspace_bytes(r1 - r0, c.Hq, c.Hkv, c.d, row)
+                            for row in self.S), dtype=torch.uint8, device=device)
+            for r0, r1 in self.parts] if mb > 1 else [self.workspace]
 
     def queries(self) -> List[torch.Tensor]:
         return [self.wl.q(l, device=self.device) for l in range(self.cfg.L)]
@@ -115,18 +128,52 @@ class DecodeStep:
         for l in range(self.cfg.L):
             self.run_layer(l, qs[l], stream)
 
+    def run_part(self, k: int, qs: List[torch.Tensor], stream) -> None:
+        """Every layer for the requests of micro-batch k, on ``stream``."""
+        c = self.cfg
+        r0, r1 = self.parts[k]
+        for l in range(c.L):
+            cache, buf, q = self.caches[l].rows(r0, r1), self.bufs[l], qs[l][r0:r1]
+            if c.topk:
+                kvs.kvs_score_pages(cache, q, buf.scores[r0:r1], stream)
+                kvs.kvs_topk_pages(buf.scores[r0:r1], cache.seq_len, c.P, c.topk,
+                                   buf.sel[r0:r1], buf.sel_count[r0:r1], stream)
+            kvs.kvs_decode_attn(cache, q, buf.sel[r0:r1] if c.topk else None,
+                                buf.sel_count[r0:r1] if c.topk else None, c.topk or 0,
+                                self.S[l], self.scale, self.part_ws[k], buf.out[r0:r1], stream)
+
     def capture(self, qs: List[torch.Tensor]) -> "torch.cuda.CUDAGraph":
         """Record one whole step (every layer) as a HIP graph.  Every launch
         has a static grid and takes its arguments by value, and the step
         issues no memset, so a replay re-runs exactly the eager step on the
-        buffers bound at capture time."""
+        buffers bound at capture time.  With several micro-batches the graph
+        forks into one stream per part and joins at the end."""
         g = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            self.run(qs, side)          # warm-up on the capture stream
-        torch.cuda.current_stream().wait_stream(side)
+        if len(self.parts) == 1:
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                self.run(qs, side)          # warm-up on the capture stream
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                self.run(qs, torch.cuda.current_stream())
+            return g
+        streams = [torch.cuda.Stream() for _ in self.parts]
+        cur = torch.cuda.current_stream()
+        for k, s in enumerate(streams):     # warm-up, eagerly, on the same streams
+            s.wait_stream(cur)
+            self.run_part(k, qs, s)
+        for s in streams:
+            cur.wait_stream(s)
         torch.cuda.synchronize()
         with torch.cuda.graph(g):
-            self.run(qs, torch.cuda.current_stream())
+            cur = torch.cuda.current_stream()
+            for s in streams:
+                s.wait_stream(cur)
+            for k, s in enumerate(streams):
+                self.run_part(k, qs, s)
+            for s in streams:
+                cur.wait_stream(s)
+        self._graph_streams = streams       # kept alive with the graph
         return g

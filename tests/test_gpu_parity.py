@@ -19,11 +19,11 @@ from non_uniform_sparse_amd.workloads import make_workload
 pytestmark = pytest.mark.gpu
 
 
-def _full(name, **ov):
+def _full(name, microbatches=1, **ov):
     require_gpu()
     wl = make_workload(name, **ov)
     say(f"[case] {name} {ov} building caches")
-    step = DecodeStep(wl, device="cuda")
+    step = DecodeStep(wl, device="cuda", microbatches=microbatches)
     say(f"[case] {name}: W={step.W} T={step.T} S[0]={step.S[0].tolist()}")
     return wl, step
 
@@ -43,7 +43,10 @@ def test_workload_full(name):
     ("gemma3_mixed", [0, 1, 32, 63], [0, 9, 24, 47]),
 ])
 def test_workload_sampled(name, requests, layers):
-    wl, step = _full(name)
+    """Full-size caches; sampled requests and layers against the oracle, and
+    the step as the bench times it (a graph of three request micro-batches
+    on three streams) bit for bit against the eager step, on every layer."""
+    wl, step = _full(name, microbatches=3)
     st = Stats()
     qs = step.queries()
     step.run(qs)                       # every layer runs, as in the bench
@@ -51,6 +54,17 @@ def test_workload_sampled(name, requests, layers):
     for l in layers:
         check_layer(step, l, qs[l], requests, st)
     assert_output_bar(st, name)
+    step.run(qs)
+    torch.cuda.synchronize()
+    ref = [b.out.clone() for b in step.bufs]
+    g = step.capture(qs)
+    for b in step.bufs:
+        b.out.fill_(float("nan"))
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    for l, b in enumerate(step.bufs):
+        assert torch.equal(b.out, ref[l]), f"micro-batched graph differs on layer {l}"
 
 
 def _split_rows(step, l):
@@ -210,12 +224,14 @@ def test_deterministic():
     assert torch.equal(a, b) and torch.equal(sel_a, step.bufs[0].sel)
 
 
-@pytest.mark.parametrize("name", ["flexicache_topk", "longctx_skew"])
-def test_graph_replay_matches_eager(name):
-    """A captured step replays to the eager result, every replay, with eager
-    work and synchronisation in between."""
+@pytest.mark.parametrize("name,mb", [("flexicache_topk", 1), ("longctx_skew", 1),
+                                     ("flexicache_topk", 3), ("longctx_skew", 2)])
+def test_graph_replay_matches_eager(name, mb):
+    """A captured step (one stream, or request micro-batches on streams of
+    their own) replays to the eager result, every replay, with eager work
+    and synchronisation in between."""
     ov = {"b": 6} if name == "flexicache_topk" else {"L": 3}
-    wl, step = _full(name, **ov)
+    wl, step = _full(name, microbatches=mb, **ov)
     qs = step.queries()
     step.run(qs)
     torch.cuda.synchronize()
