@@ -25,7 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from non_uniform_sparse_amd import kvs  # noqa: E402
-from non_uniform_sparse_amd.pipeline import DecodeStep  # noqa: E402
+from non_uniform_sparse_amd.pipeline import DecodeStep, default_microbatches  # noqa: E402
 from non_uniform_sparse_amd.workloads import CONFIGS, make_workload  # noqa: E402
 
 METRIC = "decode-attn KV GB/s (% of HBM peak) + µs/step, ragged top-K, 1 MI355X"
@@ -195,8 +195,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(CONFIGS))
-    ap.add_argument("--microbatches", type=int, default=3,
-                    help="request micro-batches, each on a stream of its own in the step graph")
+    ap.add_argument("--microbatches", type=int, default=0,
+                    help="request micro-batches, each on a stream of its own in the step graph "
+                         "(0: one below 4 layers, else min(3, requests))")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--skew", nargs="*", default=None, metavar="CONFIG",
@@ -236,7 +237,8 @@ def main() -> int:
     t0 = time.time()
     wl = make_workload(args.config)
     c = wl.cfg
-    step = DecodeStep(wl, device=dev, microbatches=args.microbatches)
+    step = DecodeStep(wl, device=dev,
+                      microbatches=args.microbatches or default_microbatches(wl))
     qs = step.queries()
     torch.cuda.synchronize()
     log(f"[bench] {c.name}: set-up {time.time() - t0:.1f} s, W={step.W}, T={step.T}, "
@@ -312,9 +314,11 @@ def main() -> int:
     wall_ms = (time.perf_counter() - wall0) * 1e3
 
     # With flushes the steps are timed one by one (the flush is not step
-    # work); without, the wall clock over the K back-to-back replays.
-    ms = (statistics.mean(a.elapsed_time(b_) for a, b_ in marks) if flush is not None
-          else wall_ms / args.steps)
+    # work); without, the wall clock over the K back-to-back replays.  The
+    # per-step events give the spread either way.
+    per_step = sorted(a.elapsed_time(b_) for a, b_ in marks)
+    ms = statistics.mean(per_step) if flush is not None else wall_ms / args.steps
+    pct = lambda f: per_step[min(len(per_step) - 1, int(f * len(per_step)))]
     dec_ms = statistics.mean(kern["decode_attn"])
     dec_bytes = statistics.mean(a["decode_launch"] for a in ab)
     achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
@@ -356,6 +360,8 @@ def main() -> int:
             "traffic": traffic,
         },
         "wall_ms_per_step_incl_flush": round(wall_ms / args.steps, 4),
+        "step_ms_p10_p50_p90": [round(pct(0.1), 4), round(statistics.median(per_step), 4),
+                                round(pct(0.9), 4)],
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host ...")

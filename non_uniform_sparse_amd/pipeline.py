@@ -27,7 +27,7 @@ from . import kvs
 from .layout import RaggedLayout, build_caches
 from .workloads import Workload, torch_dtype
 
-__all__ = ["DecodeStep", "splits_per_request", "topk_cap"]
+__all__ = ["DecodeStep", "splits_per_request", "topk_cap", "default_microbatches"]
 
 
 def splits_per_request(W: int, b: int, G: int, mean_units: float, min_units: int = 8) -> int:
@@ -37,6 +37,16 @@ def splits_per_request(W: int, b: int, G: int, mean_units: float, min_units: int
     t = W // max(1, b)
     t = min(t, max(1, math.ceil(mean_units / min_units)))
     return max(G, t)
+
+
+def default_microbatches(wl: Workload) -> int:
+    """Request micro-batches for the step graph.  Parts only overlap once
+    their layer chains drift apart; with a single layer (or a few) every part
+    runs the same phase at the same time and the split only adds launches
+    (measured: one-layer steps are fastest unsplit, 32- and 48-layer steps
+    fastest with 2-3 parts)."""
+    c = wl.cfg
+    return 1 if c.L < 4 else min(3, c.b)
 
 
 def topk_cap(wl: Workload) -> float:

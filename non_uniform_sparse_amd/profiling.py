@@ -46,15 +46,31 @@ def _short(name: str) -> str:
     return re.sub(r"\((kvs::|float|unsigned|int|const|at::).*$", "", name).strip()
 
 
+def _grid_col(cols):
+    for c in cols:
+        lc = c.lower()
+        if "grid" in lc and (lc.endswith("x") or lc == "grid_size"):
+            return cols.index(c)
+    return None
+
+
 def kernel_stats(path: str) -> dict:
+    """Durations (us) per (kernel, grid size): launches of one kernel at
+    different sizes, e.g. whole-batch and micro-batch launches, stay apart."""
     con = _db(path)
     cols = [r[1] for r in con.execute("pragma table_info(kernels)")]
     ki = cols.index("name") if "name" in cols else cols.index("kernel_name")
     st, en = cols.index("start"), cols.index("end")
+    gi = _grid_col(cols)
     agg = collections.defaultdict(list)
     for r in con.execute("select * from kernels"):
-        agg[_short(r[ki])].append((r[en] - r[st]) / 1e3)
-    return agg
+        agg[(_short(r[ki]), r[gi] if gi is not None else "")].append((r[en] - r[st]) / 1e3)
+    # a kernel launched at many sizes (one per layer, say) gets one row
+    grids = collections.Counter(name for name, _ in agg)
+    out = collections.defaultdict(list)
+    for (name, grid), v in agg.items():
+        out[(name, "various" if grids[name] > 4 else grid)].extend(v)
+    return out
 
 
 def pmc_stats(path: str) -> dict:
@@ -73,13 +89,13 @@ def _header(cmd: str) -> str:
 
 def write_trace(path: str, cmd: str, out: str, pattern: str = "kvs") -> None:
     stats = kernel_stats(path)
-    lines = [_header(cmd), f"{'kernel':64s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} "
-             f"{'max_us':>9s} {'total_ms':>9s}"]
-    for name, v in sorted(stats.items(), key=lambda x: -sum(x[1])):
+    lines = [_header(cmd), f"{'kernel':56s} {'grid':>9s} {'calls':>6s} {'avg_us':>9s} "
+             f"{'min_us':>9s} {'max_us':>9s} {'total_ms':>9s}"]
+    for (name, grid), v in sorted(stats.items(), key=lambda x: -sum(x[1])):
         if pattern and not re.search(pattern, name):
             continue
-        lines.append(f"{name[:64]:64s} {len(v):6d} {statistics.mean(v):9.2f} {min(v):9.2f} "
-                     f"{max(v):9.2f} {sum(v) / 1e3:9.2f}")
+        lines.append(f"{name[:56]:56s} {str(grid):>9s} {len(v):6d} {statistics.mean(v):9.2f} "
+                     f"{min(v):9.2f} {max(v):9.2f} {sum(v) / 1e3:9.2f}")
     open(out, "w").write("\n".join(lines) + "\n")
 
 
