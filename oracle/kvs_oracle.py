@@ -39,6 +39,9 @@ __all__ = [
     "group_units",
     "decode_group_split",
     "decode_head",
+    "rerank_due",
+    "layer_scoring_needed",
+    "decode_head_steps",
 ]
 
 
@@ -321,3 +324,62 @@ def decode_head(q_group: np.ndarray, K: np.ndarray, V: np.ndarray,
     toks = [t for p in pages for t in page_token_ids(int(p), n, P)]
     return np.stack([attention(q_group[g], K[toks], V[toks], scale)
                      for g in range(q_group.shape[0])])
+
+
+# ---------------------------------------------------------------------------
+# Decoding over steps -- FlexiCache summary, Method (head classes and the
+# stability-aware rerank schedule) and Key observations, assumption 2 (the
+# MinMax cache stays on the GPU, so a page can be scored at any step).
+# ---------------------------------------------------------------------------
+
+def rerank_due(t: int, stable: bool, period: int = 16) -> bool:
+    """Whether a head re-selects its top-K pages at decode step t.
+
+    Unstable heads re-select at every step; stable heads once every
+    ``period`` steps and reuse their previous selection in between.
+    Reading: steps are counted from the first decode step (t = 0), which
+    always selects since no earlier selection exists, so a stable head
+    re-selects at t = 0, period, 2*period, ...
+    """
+    if t < 0 or period < 1:
+        raise ValueError("t >= 0 and period >= 1 required")
+    return (not stable) or t % period == 0
+
+
+def layer_scoring_needed(t: int, stable: Sequence[bool], period: int = 16) -> bool:
+    """A layer is scored at step t only if some head of it re-selects; a
+    layer of stable heads skips scoring between its rerank steps.  This
+    never changes a result: scores of heads that do not re-select are not
+    used."""
+    return any(rerank_due(t, bool(s), period) for s in stable)
+
+
+def decode_head_steps(q_steps: np.ndarray, K0: np.ndarray, V0: np.ndarray,
+                      k_new: np.ndarray, v_new: np.ndarray, stable: bool, K: int,
+                      P: int, scale: float, period: int = 16):
+    """One KV head decoded over T steps with the rerank schedule.
+
+    Step t first appends token t (k_new[t], v_new[t]) to the head's keys and
+    values (the token being decoded is part of the cache it attends), then,
+    if ``rerank_due(t, stable, period)``, re-selects the top-K pages from the
+    min-max bounds of the pages as they now stand; otherwise it keeps the
+    pages chosen at its last rerank (pages created since are not attended
+    until the next rerank).  It then attends the current valid tokens of its
+    selected pages.
+
+    q_steps [T][Gq][d], K0/V0 [n0][d], k_new/v_new [T][d], all float64.
+    Returns (outputs [T][Gq][d], selections: list of T page arrays).
+    """
+    Kc = np.asarray(K0, dtype=np.float64)
+    Vc = np.asarray(V0, dtype=np.float64)
+    sel = None
+    outs, sels = [], []
+    for t in range(q_steps.shape[0]):
+        Kc = np.concatenate([Kc, np.asarray(k_new[t], dtype=np.float64)[None]])
+        Vc = np.concatenate([Vc, np.asarray(v_new[t], dtype=np.float64)[None]])
+        if rerank_due(t, stable, period):
+            kmin, kmax = page_minmax(Kc, P)
+            sel = topk_pages(page_scores(q_steps[t], kmin, kmax), K)
+        outs.append(decode_head(q_steps[t], Kc, Vc, sel, P, scale))
+        sels.append(np.array(sel, dtype=np.int64))
+    return np.stack(outs), sels

@@ -393,3 +393,72 @@ def test_split_bounds_floor_convention():
     # split s starts at floor(s U / S): 5 units over 3 splits -> sizes 1, 2, 2
     assert O.split_bounds(5, 3) == [(0, 1), (1, 3), (3, 5)]
     assert O.split_bounds(2, 4) == [(0, 0), (0, 1), (1, 1), (1, 2)]
+
+
+# ------------------------------------------------ decoding over steps ------
+
+def test_rerank_schedule_counts():
+    """Stable heads re-select at t = 0, period, 2 period, ...; unstable heads
+    every step; a layer of stable heads is scored only at those steps."""
+    T = 48
+    assert [t for t in range(T) if O.rerank_due(t, True, 16)] == [0, 16, 32]
+    assert all(O.rerank_due(t, False, 16) for t in range(T))
+    assert all(O.rerank_due(t, True, 1) for t in range(T))
+    assert [t for t in range(T) if O.layer_scoring_needed(t, [True] * 8, 16)] == [0, 16, 32]
+    assert all(O.layer_scoring_needed(t, [True] * 7 + [False], 16) for t in range(T))
+    with pytest.raises(ValueError):
+        O.rerank_due(-1, True)
+
+
+@pytest.mark.parametrize("kind", ["stable", "unstable"])
+def test_decode_steps_golden(kind):
+    g = GOLD["rerank_reuse"]
+    outs, sels = O.decode_head_steps(np.array(g["q_steps"]), np.array(g["K0"]), np.array(g["V0"]),
+                                     np.array(g["k_new"]), np.array(g["v_new"]), kind == "stable",
+                                     g["K"], g["P"], g["scale"], g["period"])
+    assert np.allclose(outs[:, 0, 0], [o[0] for o in g[kind]["o"]], rtol=1e-14, atol=0)
+    assert [s.tolist() for s in sels] == g[kind]["sel"]
+
+
+def _dense(q, K, V, scale):
+    z = (K @ q) * scale
+    w = np.exp(z - z.max())
+    return (w[:, None] * V).sum(axis=0) / w.sum()
+
+
+def test_decode_steps_full_budget_every_step_is_dense():
+    """With K covering every page and a re-selection at every step, each step
+    is dense attention over all tokens held so far, the new one included."""
+    rng = np.random.default_rng(5)
+    P, d, Gq, T, n0 = 4, 3, 2, 9, 6
+    K0, V0 = rng.normal(size=(n0, d)), rng.normal(size=(n0, d))
+    kn, vn = rng.normal(size=(T, d)), rng.normal(size=(T, d))
+    q = rng.normal(size=(T, Gq, d))
+    outs, sels = O.decode_head_steps(q, K0, V0, kn, vn, False, 100, P, 0.7, 16)
+    for t in range(T):
+        Kt, Vt = np.vstack([K0, kn[:t + 1]]), np.vstack([V0, vn[:t + 1]])
+        assert sels[t].tolist() == list(range(-(-(n0 + t + 1) // P)))
+        for g in range(Gq):
+            assert np.allclose(outs[t, g], _dense(q[t, g], Kt, Vt, 0.7), rtol=1e-12, atol=1e-14)
+
+
+def test_decode_steps_stable_head_keeps_stale_pages():
+    """Between reranks a stable head attends exactly the pages chosen at its
+    last rerank, with the tokens those pages hold now; pages created later
+    are not attended."""
+    rng = np.random.default_rng(9)
+    P, d, T, n0, K = 4, 2, 12, 7, 2
+    K0, V0 = rng.normal(size=(n0, d)), rng.normal(size=(n0, d))
+    kn, vn = rng.normal(size=(T, d)) + 4.0, rng.normal(size=(T, d))
+    q = np.ones((T, 1, d))
+    outs, sels = O.decode_head_steps(q, K0, V0, kn, vn, True, K, P, 1.0, 16)
+    first = sels[0].tolist()
+    assert all(s.tolist() == first for s in sels)
+    for t in range(1, T):
+        n = n0 + t + 1
+        Kt, Vt = np.vstack([K0, kn[:t + 1]]), np.vstack([V0, vn[:t + 1]])
+        toks = [i for p in first for i in range(p * P, min(n, (p + 1) * P))]
+        assert np.allclose(outs[t, 0], _dense(q[t, 0], Kt[toks], Vt[toks], 1.0), rtol=1e-12)
+    # an unstable head sees the new high-key pages instead
+    _, sels_u = O.decode_head_steps(q, K0, V0, kn, vn, False, K, P, 1.0, 16)
+    assert sels_u[-1].tolist() != first
