@@ -130,6 +130,58 @@ def cpu_baseline(wl, step, budget_s: float = 12.0) -> dict:
                       f"{done_bytes / 1e6:.1f} MB of KV in {spent:.1f} s"}
 
 
+def rerank_reuse_report(configs, period: int = 16, unstable_frac: float = 0.25,
+                        reps: int = 10) -> dict:
+    """Decoding over steps with stability-aware reranking against reranking
+    every head every step (FlexiCache summary, Method; the summary's decode
+    microbenchmark compares the two).  Both variants run the same window of
+    ``period`` steps -- append, [score + top-K], decode -- captured as one
+    graph and replayed from the same starting state; a window costs one
+    full rerank plus period - 1 steps in which only unstable heads re-select.
+    Windows of small working sets are preceded by a 1 GiB read, as in the
+    headline protocol."""
+    from non_uniform_sparse_amd.steps import DecodeLoop
+    out = {}
+    for name in configs:
+        ov = {"L": 8} if name == "gemma3_mixed" else {}
+        wl = make_workload(name, **ov)
+        loop = DecodeLoop(wl, period, device="cuda", period=period, unstable_frac=unstable_frac,
+                          poison=False)
+        c = wl.cfg
+        npg = -(-wl.n // c.P)                                   # [b][L][Hkv]
+        small = (np.minimum(npg, c.topk).sum() * 2 * c.P + npg.sum() * 2) * c.d * 2 < 8e9
+        flush = torch.ones(1 << 27, dtype=torch.int64, device="cuda") if small else None
+        res = {}
+        for mode, reuse in (("reuse", True), ("every_step", False)):
+            g = loop.capture(period, reuse=reuse)
+            times = []
+            for _ in range(reps + 2):
+                loop.rewind()
+                if flush is not None:
+                    flush.sum()
+                a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                g.replay()
+                b_.record()
+                b_.synchronize()
+                times.append(a.elapsed_time(b_) / period * 1e3)
+            res[mode] = statistics.median(times[2:])
+            del g
+        unstable = int((~loop.stable).sum())
+        out[name] = {
+            "layers": c.L, "requests": c.b, "topk_pages": c.topk, "period": period,
+            "unstable_heads": f"{unstable} of {c.L * c.Hkv}",
+            "all_stable_layers": int(loop.stable.all(axis=1).sum()),
+            "us_per_step_reuse": round(res["reuse"], 1),
+            "us_per_step_every_step": round(res["every_step"], 1),
+            "speedup": round(res["every_step"] / res["reuse"], 3),
+            "includes": "append + scoring/top-K of the heads due + decode, per step",
+        }
+        del loop
+        torch.cuda.empty_cache()
+    return out
+
+
 def skew_report(configs, launches: int = 20) -> dict:
     """Per-workgroup duration skew of the split-K decode kernel, max / mean
     over the workgroups of one launch, median over launches, per layer; with
@@ -199,6 +251,10 @@ def main() -> int:
                     help="request micro-batches, each on a stream of its own in the step graph "
                          "(0: one below 4 layers, else min(3, requests))")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rerank-reuse", nargs="*", default=None, metavar="CONFIG",
+                    help="time decoding over steps with stability-aware reranking against "
+                         "reranking every step (default configs: flexicache_topk, gemma3_mixed "
+                         "at 8 layers) and print that record instead of the step line")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--skew", nargs="*", default=None, metavar="CONFIG",
                     help="measure per-workgroup duration skew (planned vs uniform split "
@@ -214,6 +270,10 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.rerank_reuse is not None:
+        print(json.dumps({"rerank_reuse": rerank_reuse_report(
+            args.rerank_reuse or ["flexicache_topk", "gemma3_mixed"])}))
+        return 0
     if args.skew is not None:
         print(json.dumps({"skew": skew_report(args.skew or ["llama8b_ragged", "longctx_skew"])}))
         return 0

@@ -9,9 +9,11 @@
  *       3.2 Ragged Paging, 3.3 AOT Load Balancing.
  *   [F] "FlexiCache: Leveraging Temporal Stability of Attention Heads for
  *       Efficient KV Cache Management (MLSys 2026)" (paper summary): Core
- *       method (sparse decode, Quest-style min-max page bound), System
- *       engineering (per-head-layer block table with null blocks), Key
- *       observations, assumption 2 (GPU-resident MinMax cache).
+ *       method (sparse decode, Quest-style min-max page bound), Method
+ *       (stable and unstable heads, rerank every 16 steps for stable heads,
+ *       no scoring between reranks), System engineering (per-head-layer
+ *       block table with null blocks), Key observations, assumption 2
+ *       (GPU-resident MinMax cache).
  *
  * Conventions shared by every call
  *   - Return value: KVS_OK (0) or a negative KVS_E* code.  On error no kernel
@@ -64,7 +66,8 @@ enum { KVS_F16 = 0, KVS_BF16 = 1 };
  * A group is allocated pages for its longest head [T 3.2]; shorter heads of
  * the group leave the tail of their slots unused.
  *
- *   kv          device, [num_pages][Hp][2][P][d] dtype.
+ *   kv          device, [num_pages][Hp][2][P][d] dtype.  Written only by
+ *               kvs_append_kv.
  *   minmax      device, [num_meta][d][2] dtype: the min-max cache [F Key
  *               observations, assumption 2], kept apart from the KV pages
  *               and ragged per head: block meta_base[r][h] + p holds, for
@@ -79,8 +82,9 @@ enum { KVS_F16 = 0, KVS_BF16 = 1 };
  *               -1 marks a null entry [F System engineering].  Logical page
  *               p of head h covers its tokens [p*P, (p+1)*P).
  *   seq_len     device, [b][Hkv] int32: n, the tokens head h of request r
- *               retained (ceil(B*N) under Budget Reservation [T 3.1]),
- *               1 <= n <= P*max_group_pages.
+ *               holds (ceil(B*N) retained under Budget Reservation [T 3.1],
+ *               plus the tokens appended since), 1 <= n <= P*max_group_pages.
+ *               Written only by kvs_append_kv.
  *   head_slot   device, [Hkv] int32: head h sits in group head_slot[h]/Hp,
  *               slot head_slot[h]%Hp; a permutation of [0, Hkv).
  *   b, Hq, Hkv  requests, query heads, KV heads (Hq % Hkv == 0).
@@ -91,11 +95,11 @@ enum { KVS_F16 = 0, KVS_BF16 = 1 };
  *   dtype       KVS_F16 or KVS_BF16.
  */
 typedef struct kvs_paged_kv {
-  const void* kv;
+  void* kv;
   void* minmax;
   const int32_t* meta_base;
   const int32_t* page_table;
-  const int32_t* seq_len;
+  int32_t* seq_len;
   const int32_t* head_slot;
   int32_t b, Hq, Hkv, Hp, d, P, max_group_pages, num_pages, num_meta, dtype;
 } kvs_paged_kv;
@@ -128,6 +132,16 @@ int kvs_build_minmax(const kvs_paged_kv* cache, void* stream);
 int kvs_score_pages(const kvs_paged_kv* cache, const void* q, float* scores, void* stream);
 
 /*
+ * kvs_score_pages restricted to the KV heads h with heads[h] != 0 (host
+ * array [Hkv], the same for every request): stable heads are not scored
+ * between their reranks, and a layer whose heads are all stable is not
+ * scored at all [F Method].  Score rows of the other heads are left
+ * untouched.  The heads array is read before the call returns.
+ */
+int kvs_score_pages_heads(const kvs_paged_kv* cache, const void* q, const uint8_t* heads,
+                          float* scores, void* stream);
+
+/*
  * Per-KV-head top-K page selection [F Core method].  For each (r, h) with
  * np = ceil(seq_len[r][h]/P) pages: keep the min(K, np) pages of largest
  * score, equal scores going to the lower page index, and write them in
@@ -142,6 +156,32 @@ int kvs_score_pages(const kvs_paged_kv* cache, const void* q, float* scores, voi
 int kvs_topk_pages(const float* scores, const int32_t* seq_len, int32_t P, int32_t b,
                    int32_t Hkv, int32_t max_pages, int32_t K, int32_t* sel,
                    int32_t* sel_count, void* stream);
+
+/*
+ * kvs_topk_pages restricted to the KV heads h with heads[h] != 0 (host array
+ * [Hkv]); the other heads keep the selection they hold, sel and sel_count
+ * untouched -- a stable head reuses the pages of its last rerank [F Method].
+ */
+int kvs_topk_pages_heads(const float* scores, const int32_t* seq_len, int32_t P, int32_t b,
+                         int32_t Hkv, int32_t max_pages, int32_t K, const uint8_t* heads,
+                         int32_t* sel, int32_t* sel_count, void* stream);
+
+/*
+ * Append the decoded token of every head to its ragged page [F Method: the
+ * token being decoded joins the cache; T 3.2 Ragged Paging] and update that
+ * page's min-max bounds in place [F Key observations, assumption 2].  For
+ * every (r, h) with n = seq_len[r][h] < P*max_group_pages: K and V of the
+ * token go to row n % P of logical page p = n / P in the head's slot;
+ * block meta_base[r][h] + p becomes (k, k) per channel if the row is the
+ * page's first, else (min(kmin, k), max(kmax, k)) (exact: a selection);
+ * then seq_len[r][h] = n + 1.
+ *   k_new, v_new  device, [b][Hkv][d] dtype, 16-byte aligned.
+ * The caller maps page p in the page table and owns block meta_base[r][h] +
+ * p before the call.  A head whose page entry is null or outside the pool,
+ * whose block lies outside [0, num_meta), or whose n is already
+ * P*max_group_pages is left as it is (token, bounds and n unchanged).
+ */
+int kvs_append_kv(const kvs_paged_kv* cache, const void* k_new, const void* v_new, void* stream);
 
 /*
  * Ahead-of-time workload split map [T 3.3], host only.

@@ -108,41 +108,101 @@ extern "C" int kvs_build_minmax(const kvs_paged_kv* cache, void* stream) {
   return KVS_OK;
 }
 
+namespace {
+HeadMask every_head() {
+  HeadMask m{};
+  m.all = 1u;
+  return m;
+}
+
+// The heads h < Hkv with heads[h] != 0 (host array), or an error.
+int head_subset(const uint8_t* heads, int Hkv, HeadMask* m, const char* fn) {
+  if (!heads) return set_error(KVS_EINVAL, "%s: heads is NULL", fn);
+  if (Hkv > kMaxHkv) return set_error(KVS_EUNSUPPORTED, "%s: Hkv=%d > %d", fn, Hkv, kMaxHkv);
+  *m = HeadMask{};
+  for (int h = 0; h < Hkv; ++h)
+    if (heads[h]) m->w[h >> 5] |= 1u << (h & 31);
+  return KVS_OK;
+}
+
+int score_impl(const kvs_paged_kv* cache, const void* q, float* scores, const HeadMask& heads,
+               void* stream, const char* fn) {
+  CacheView c;
+  if (int rc = check_cache(cache, true, fn, &c)) return rc;
+  if (!q || !scores) return set_error(KVS_EINVAL, "%s: null q or scores", fn);
+  if (!aligned16(q)) return set_error(KVS_EINVAL, "%s: q must be 16-byte aligned", fn);
+  if ((int64_t)c.b * c.Hkv > kMaxScoreHeads)
+    return set_error(KVS_EUNSUPPORTED, "%s: b*Hkv=%lld > %d", fn, (long long)c.b * c.Hkv,
+                     kMaxScoreHeads);
+  if ((int64_t)c.b * c.Hkv * c.maxpg > 0x7fffffff)
+    return set_error(KVS_EUNSUPPORTED, "%s: b*Hkv*max_group_pages >= 2^31", fn);
+  if (hipError_t e = launch_score(c, q, scores, heads, (hipStream_t)stream)) return hip_error(e, fn);
+  return KVS_OK;
+}
+
+int topk_impl(const float* scores, const int32_t* seq_len, int32_t P, int32_t b, int32_t Hkv,
+              int32_t max_pages, int32_t K, const HeadMask& heads, int32_t* sel,
+              int32_t* sel_count, void* stream, const char* fn) {
+  if (!scores || !seq_len || !sel || !sel_count) return set_error(KVS_EINVAL, "%s: null pointer", fn);
+  if (P != 16) return set_error(KVS_EUNSUPPORTED, "%s: page size %d != 16", fn, P);
+  if (b < 1 || Hkv < 1 || max_pages < 1)
+    return set_error(KVS_EINVAL, "%s: sizes must be positive", fn);
+  if (K < 1 || K > kMaxK) return set_error(KVS_EINVAL, "%s: K=%d not in [1, %d]", fn, K, kMaxK);
+  if (max_pages > kMaxTopkPages)
+    return set_error(KVS_EUNSUPPORTED, "%s: max_pages=%d > %d", fn, max_pages, kMaxTopkPages);
+  if ((int64_t)b * Hkv > 0x7fffffff) return set_error(KVS_EINVAL, "%s: b*Hkv too large", fn);
+  if (hipError_t e = launch_topk(scores, seq_len, P, b, Hkv, max_pages, K, heads, sel, sel_count,
+                                 (hipStream_t)stream))
+    return hip_error(e, fn);
+  return KVS_OK;
+}
+}  // namespace
+
 extern "C" int kvs_score_pages(const kvs_paged_kv* cache, const void* q, float* scores,
                                void* stream) {
   clear_error();
-  CacheView c;
-  if (int rc = check_cache(cache, true, "kvs_score_pages", &c)) return rc;
-  if (!q || !scores) return set_error(KVS_EINVAL, "kvs_score_pages: null q or scores");
-  if (!aligned16(q)) return set_error(KVS_EINVAL, "kvs_score_pages: q must be 16-byte aligned");
-  if ((int64_t)c.b * c.Hkv > kMaxScoreHeads)
-    return set_error(KVS_EUNSUPPORTED, "kvs_score_pages: b*Hkv=%lld > %d", (long long)c.b * c.Hkv,
-                     kMaxScoreHeads);
-  if ((int64_t)c.b * c.Hkv * c.maxpg > 0x7fffffff)
-    return set_error(KVS_EUNSUPPORTED, "kvs_score_pages: b*Hkv*max_group_pages >= 2^31");
-  if (hipError_t e = launch_score(c, q, scores, (hipStream_t)stream))
-    return hip_error(e, "kvs_score_pages");
-  return KVS_OK;
+  return score_impl(cache, q, scores, every_head(), stream, "kvs_score_pages");
+}
+
+extern "C" int kvs_score_pages_heads(const kvs_paged_kv* cache, const void* q,
+                                     const uint8_t* heads, float* scores, void* stream) {
+  clear_error();
+  static const char* fn = "kvs_score_pages_heads";
+  if (!cache) return set_error(KVS_EINVAL, "%s: cache descriptor is NULL", fn);
+  HeadMask m;
+  if (int rc = head_subset(heads, cache->Hkv, &m, fn)) return rc;
+  return score_impl(cache, q, scores, m, stream, fn);
 }
 
 extern "C" int kvs_topk_pages(const float* scores, const int32_t* seq_len, int32_t P, int32_t b,
                               int32_t Hkv, int32_t max_pages, int32_t K, int32_t* sel,
                               int32_t* sel_count, void* stream) {
   clear_error();
-  if (!scores || !seq_len || !sel || !sel_count)
-    return set_error(KVS_EINVAL, "kvs_topk_pages: null pointer");
-  if (P != 16) return set_error(KVS_EUNSUPPORTED, "kvs_topk_pages: page size %d != 16", P);
-  if (b < 1 || Hkv < 1 || max_pages < 1)
-    return set_error(KVS_EINVAL, "kvs_topk_pages: sizes must be positive");
-  if (K < 1 || K > kMaxK)
-    return set_error(KVS_EINVAL, "kvs_topk_pages: K=%d not in [1, %d]", K, kMaxK);
-  if (max_pages > kMaxTopkPages)
-    return set_error(KVS_EUNSUPPORTED, "kvs_topk_pages: max_pages=%d > %d", max_pages,
-                     kMaxTopkPages);
-  if ((int64_t)b * Hkv > 0x7fffffff) return set_error(KVS_EINVAL, "kvs_topk_pages: b*Hkv too large");
-  if (hipError_t e = launch_topk(scores, seq_len, P, b, Hkv, max_pages, K, sel, sel_count,
-                                 (hipStream_t)stream))
-    return hip_error(e, "kvs_topk_pages");
+  return topk_impl(scores, seq_len, P, b, Hkv, max_pages, K, every_head(), sel, sel_count, stream,
+                   "kvs_topk_pages");
+}
+
+extern "C" int kvs_topk_pages_heads(const float* scores, const int32_t* seq_len, int32_t P,
+                                    int32_t b, int32_t Hkv, int32_t max_pages, int32_t K,
+                                    const uint8_t* heads, int32_t* sel, int32_t* sel_count,
+                                    void* stream) {
+  clear_error();
+  static const char* fn = "kvs_topk_pages_heads";
+  HeadMask m;
+  if (int rc = head_subset(heads, Hkv, &m, fn)) return rc;
+  return topk_impl(scores, seq_len, P, b, Hkv, max_pages, K, m, sel, sel_count, stream, fn);
+}
+
+extern "C" int kvs_append_kv(const kvs_paged_kv* cache, const void* k_new, const void* v_new,
+                             void* stream) {
+  clear_error();
+  static const char* fn = "kvs_append_kv";
+  CacheView c;
+  if (int rc = check_cache(cache, true, fn, &c)) return rc;
+  if (!k_new || !v_new) return set_error(KVS_EINVAL, "%s: null k_new or v_new", fn);
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return set_error(KVS_EINVAL, "%s: k_new and v_new must be 16-byte aligned", fn);
+  if (hipError_t e = launch_append(c, k_new, v_new, (hipStream_t)stream)) return hip_error(e, fn);
   return KVS_OK;
 }
 

@@ -25,13 +25,23 @@ void clear_error();
 
 // A validated kvs_paged_kv with derived sizes.
 struct CacheView {
-  const void* kv;
+  void* kv;
   void* minmax;
   const int32_t* meta_base;
   const int32_t* page_table;
-  const int32_t* seq_len;
+  int32_t* seq_len;
   const int32_t* head_slot;
   int b, Hq, Hkv, Hp, G, Gq, d, P, maxpg, num_pages, num_meta, dtype;
+};
+
+// A set of KV heads, passed to kernels by value: every head, or the heads
+// whose bit is set (bit h = head h, h < kMaxHkv).
+struct HeadMask {
+  uint32_t all;
+  uint32_t w[kMaxHkv / 32];
+  __host__ __device__ bool has(int h) const {
+    return all != 0u || (h >= 0 && h < kMaxHkv && ((w[h >> 5] >> (h & 31)) & 1u));
+  }
 };
 
 struct DecodeArgs {
@@ -53,9 +63,12 @@ struct DecodeArgs {
 };
 
 hipError_t launch_minmax(const CacheView& c, hipStream_t s);
-hipError_t launch_score(const CacheView& c, const void* q, float* scores, hipStream_t s);
+hipError_t launch_score(const CacheView& c, const void* q, float* scores, const HeadMask& heads,
+                        hipStream_t s);
 hipError_t launch_topk(const float* scores, const int32_t* seq_len, int P, int b, int Hkv,
-                       int max_pages, int K, int32_t* sel, int32_t* sel_count, hipStream_t s);
+                       int max_pages, int K, const HeadMask& heads, int32_t* sel,
+                       int32_t* sel_count, hipStream_t s);
+hipError_t launch_append(const CacheView& c, const void* k_new, const void* v_new, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s);
 // Resident decode workgroups per compute unit for a kernel variant.

@@ -46,8 +46,10 @@ __device__ __forceinline__ uint32_t pick_selector(uint32_t q_pair) {
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-__device__ __forceinline__ int page_count(const CacheView& c, int rh) {
+// Pages of head rh to score: 0 for a head outside the set.
+__device__ __forceinline__ int page_count(const CacheView& c, const HeadMask& heads, int rh) {
   constexpr int P = 16;
+  if (!heads.has(rh % c.Hkv)) return 0;
   return (clampi(c.seq_len[rh], 0, P * c.maxpg) + P - 1) / P;
 }
 
@@ -55,14 +57,14 @@ __device__ __forceinline__ int page_count(const CacheView& c, int rh) {
 // pre[b * Hkv] is the total.  The page counts are first loaded into pre[]
 // with coalesced loads, up to 8 in flight per thread, then summed per
 // contiguous chunk, scanned, and overwritten in place by the prefix.
-__device__ void page_prefix(const CacheView& c, int* pre, int* part) {
+__device__ void page_prefix(const CacheView& c, const HeadMask& heads, int* pre, int* part) {
   const int BH = c.b * c.Hkv;
   const int tid = threadIdx.x;
   constexpr int CH = 8;
   for (int base = 0; base < BH; base += kThreads * CH) {
     int v[CH];
 #pragma unroll
-    for (int j = 0; j < CH; ++j) v[j] = page_count(c, min(base + j * kThreads + tid, BH - 1));
+    for (int j = 0; j < CH; ++j) v[j] = page_count(c, heads, min(base + j * kThreads + tid, BH - 1));
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       const int i = base + j * kThreads + tid;
@@ -109,14 +111,14 @@ __device__ void page_prefix(const CacheView& c, int* pre, int* part) {
 
 template <int D, int GQ, typename DT>
 __global__ __launch_bounds__(kThreads) void score_kernel(CacheView c, const uint16_t* __restrict__ q,
-                                                         float* __restrict__ scores) {
+                                                         float* __restrict__ scores, HeadMask heads) {
   constexpr int LOADS = D / 32;           // 16-byte loads per lane per page
   constexpr int PPW = 8;                  // pages per step (8 lanes each)
   constexpr int UNROLL = 16 / LOADS;      // steps per round: 64 data registers
   constexpr int RP = PPW * UNROLL;        // pages per round
   extern __shared__ int pre[];
   __shared__ int part[kThreads];
-  page_prefix(c, pre, part);
+  page_prefix(c, heads, pre, part);
 
   const int BH = c.b * c.Hkv;
   const int lane = threadIdx.x & 63;
@@ -214,8 +216,9 @@ __global__ __launch_bounds__(kThreads) void score_kernel(CacheView c, const uint
     while (hh < BH && uni(pre[hh + 1]) <= t0) ++hh;
   }
 
-  // -inf past each head's pages
+  // -inf past each head's pages (heads outside the set keep their rows)
   for (int rh = blockIdx.x; rh < BH; rh += gridDim.x) {
+    if (!heads.has(rh % c.Hkv)) continue;
     const int npg = pre[rh + 1] - pre[rh];
     float* out = scores + (int64_t)rh * c.maxpg;
     for (int p = npg + (int)threadIdx.x; p < c.maxpg; p += kThreads) out[p] = -__builtin_inff();
@@ -223,7 +226,8 @@ __global__ __launch_bounds__(kThreads) void score_kernel(CacheView c, const uint
 }
 
 template <int D, int GQ, typename DT>
-hipError_t launch_v(const CacheView& c, const void* q, float* scores, hipStream_t s) {
+hipError_t launch_v(const CacheView& c, const void* q, float* scores, const HeadMask& heads,
+                    hipStream_t s) {
   // One resident wave per slot: compute units x resident blocks per unit,
   // found once per device.
   static std::atomic<int> grid_of[kMaxDevices];
@@ -243,26 +247,30 @@ hipError_t launch_v(const CacheView& c, const void* q, float* scores, hipStream_
   }
   const size_t lds = (size_t)(c.b * c.Hkv + 1) * sizeof(int);
   hipLaunchKernelGGL((score_kernel<D, GQ, DT>), dim3((unsigned)grid), dim3(kThreads), lds, s, c,
-                     static_cast<const uint16_t*>(q), scores);
+                     static_cast<const uint16_t*>(q), scores, heads);
   return hipGetLastError();
 }
 
 template <int D, typename DT>
-hipError_t launch_g(const CacheView& c, const void* q, float* scores, hipStream_t s) {
+hipError_t launch_g(const CacheView& c, const void* q, float* scores, const HeadMask& heads,
+                    hipStream_t s) {
   switch (c.Gq) {
-    case 1: return launch_v<D, 1, DT>(c, q, scores, s);
-    case 2: return launch_v<D, 2, DT>(c, q, scores, s);
-    case 4: return launch_v<D, 4, DT>(c, q, scores, s);
-    default: return launch_v<D, 8, DT>(c, q, scores, s);
+    case 1: return launch_v<D, 1, DT>(c, q, scores, heads, s);
+    case 2: return launch_v<D, 2, DT>(c, q, scores, heads, s);
+    case 4: return launch_v<D, 4, DT>(c, q, scores, heads, s);
+    default: return launch_v<D, 8, DT>(c, q, scores, heads, s);
   }
 }
 
 }  // namespace
 
-hipError_t launch_score(const CacheView& c, const void* q, float* scores, hipStream_t s) {
+hipError_t launch_score(const CacheView& c, const void* q, float* scores, const HeadMask& heads,
+                        hipStream_t s) {
   if (c.dtype == KVS_F16)
-    return c.d == 128 ? launch_g<128, F16>(c, q, scores, s) : launch_g<256, F16>(c, q, scores, s);
-  return c.d == 128 ? launch_g<128, BF16>(c, q, scores, s) : launch_g<256, BF16>(c, q, scores, s);
+    return c.d == 128 ? launch_g<128, F16>(c, q, scores, heads, s)
+                      : launch_g<256, F16>(c, q, scores, heads, s);
+  return c.d == 128 ? launch_g<128, BF16>(c, q, scores, heads, s)
+                    : launch_g<256, BF16>(c, q, scores, heads, s);
 }
 
 }  // namespace kvs

@@ -70,7 +70,8 @@ __device__ __forceinline__ void block_minmax(int lo, int hi, int* red, int* out_
 
 __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ scores,
                                                         const int32_t* __restrict__ seq_len, int P,
-                                                        int max_pages, int K,
+                                                        int max_pages, int K, int Hkv,
+                                                        HeadMask heads,
                                                         int32_t* __restrict__ sel,
                                                         int32_t* __restrict__ sel_count) {
   extern __shared__ uint32_t keys[];   // [max_pages]
@@ -78,6 +79,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   __shared__ int red[2 * kWaves];
   __shared__ int s_digit, s_need;
   const int rh = blockIdx.x;
+  if (!heads.has(rh % Hkv)) return;   // a head outside the set keeps its selection
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int n = clampi(seq_len[rh], 0, P * max_pages);
   const int npg = (n + P - 1) / P;
@@ -199,10 +201,11 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
 }  // namespace
 
 hipError_t launch_topk(const float* scores, const int32_t* seq_len, int P, int b, int Hkv,
-                       int max_pages, int K, int32_t* sel, int32_t* sel_count, hipStream_t s) {
+                       int max_pages, int K, const HeadMask& heads, int32_t* sel,
+                       int32_t* sel_count, hipStream_t s) {
   const size_t lds = (size_t)max_pages * sizeof(uint32_t);
   hipLaunchKernelGGL(topk_kernel, dim3((unsigned)(b * Hkv)), dim3(kThreads), lds, s, scores, seq_len, P,
-                     max_pages, K, sel, sel_count);
+                     max_pages, K, Hkv, heads, sel, sel_count);
   return hipGetLastError();
 }
 

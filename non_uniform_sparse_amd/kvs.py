@@ -24,9 +24,10 @@ KVS_F16, KVS_BF16 = 0, 1
 
 # Every symbol include/kvs.h declares.
 EXPORTS = (
-    "kvs_build_minmax", "kvs_score_pages", "kvs_topk_pages", "kvs_plan_split",
-    "kvs_decode_attn", "kvs_decode_workspace_bytes", "kvs_decode_concurrency",
-    "kvs_cluster_heads", "kvs_last_error",
+    "kvs_build_minmax", "kvs_score_pages", "kvs_score_pages_heads", "kvs_topk_pages",
+    "kvs_topk_pages_heads", "kvs_append_kv", "kvs_plan_split", "kvs_decode_attn",
+    "kvs_decode_workspace_bytes", "kvs_decode_concurrency", "kvs_cluster_heads",
+    "kvs_last_error",
 )
 
 
@@ -75,7 +76,10 @@ def lib() -> ctypes.CDLL:
         pkv = ctypes.POINTER(PagedKV)
         L.kvs_build_minmax.argtypes = [pkv, vp]
         L.kvs_score_pages.argtypes = [pkv, vp, vp, vp]
+        L.kvs_score_pages_heads.argtypes = [pkv, vp, vp, vp, vp]
         L.kvs_topk_pages.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
+        L.kvs_topk_pages_heads.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
+        L.kvs_append_kv.argtypes = [pkv, vp, vp, vp]
         L.kvs_plan_split.argtypes = [vp, vp, i32, i32, i32, f64, i32, vp]
         L.kvs_decode_attn.argtypes = [pkv, vp, vp, vp, i32, vp, f32, vp, ctypes.c_size_t, vp, vp]
         L.kvs_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, vp, i32]
@@ -166,22 +170,55 @@ def kvs_build_minmax(cache: Cache, stream=None) -> None:
     _check(lib().kvs_build_minmax(ctypes.byref(s), _stream(stream)))
 
 
-def kvs_score_pages(cache: Cache, q: torch.Tensor, scores: torch.Tensor, stream=None) -> None:
+def _heads(heads, Hkv: int) -> np.ndarray:
+    h = np.ascontiguousarray(np.asarray(heads, dtype=bool).astype(np.uint8))
+    if h.shape != (Hkv,):
+        raise ValueError(f"heads must have one entry per KV head ({Hkv})")
+    return h
+
+
+def kvs_score_pages(cache: Cache, q: torch.Tensor, scores: torch.Tensor, stream=None,
+                    heads=None) -> None:
+    """Score every page (heads=None) or only those of the KV heads with
+    heads[h] true; the other heads' rows are left as they are."""
     s = cache.struct()
     _need(q, "q", (s.b, s.Hq, s.d), cache.kv.dtype, cache.kv.device)
     _need(scores, "scores", (s.b, s.Hkv, s.max_group_pages), torch.float32, cache.kv.device)
-    _check(lib().kvs_score_pages(ctypes.byref(s), _ptr(q), _ptr(scores), _stream(stream)))
+    if heads is None:
+        _check(lib().kvs_score_pages(ctypes.byref(s), _ptr(q), _ptr(scores), _stream(stream)))
+    else:
+        h = _heads(heads, s.Hkv)
+        _check(lib().kvs_score_pages_heads(ctypes.byref(s), _ptr(q), h.ctypes.data, _ptr(scores),
+                                           _stream(stream)))
 
 
 def kvs_topk_pages(scores: torch.Tensor, seq_len: torch.Tensor, P: int, K: int,
-                   sel: torch.Tensor, sel_count: torch.Tensor, stream=None) -> None:
+                   sel: torch.Tensor, sel_count: torch.Tensor, stream=None, heads=None) -> None:
+    """Top-K of every head (heads=None) or only of the KV heads with heads[h]
+    true; the other heads keep their selection."""
     b, Hkv, max_pages = scores.shape
     _need(scores, "scores", (b, Hkv, max_pages), torch.float32)
     _need(seq_len, "seq_len", (b, Hkv), torch.int32, scores.device)
     _need(sel, "sel", (b, Hkv, K), torch.int32, scores.device)
     _need(sel_count, "sel_count", (b, Hkv), torch.int32, scores.device)
-    _check(lib().kvs_topk_pages(_ptr(scores), _ptr(seq_len), P, b, Hkv, max_pages, K, _ptr(sel),
-                                _ptr(sel_count), _stream(stream)))
+    if heads is None:
+        _check(lib().kvs_topk_pages(_ptr(scores), _ptr(seq_len), P, b, Hkv, max_pages, K,
+                                    _ptr(sel), _ptr(sel_count), _stream(stream)))
+    else:
+        h = _heads(heads, Hkv)
+        _check(lib().kvs_topk_pages_heads(_ptr(scores), _ptr(seq_len), P, b, Hkv, max_pages, K,
+                                          h.ctypes.data, _ptr(sel), _ptr(sel_count),
+                                          _stream(stream)))
+
+
+def kvs_append_kv(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor, stream=None) -> None:
+    """Append one token per (request, KV head) and update its page's bounds;
+    advances the cache's seq_len on the device."""
+    s = cache.struct()
+    dev = cache.kv.device
+    _need(k_new, "k_new", (s.b, s.Hkv, s.d), cache.kv.dtype, dev)
+    _need(v_new, "v_new", (s.b, s.Hkv, s.d), cache.kv.dtype, dev)
+    _check(lib().kvs_append_kv(ctypes.byref(s), _ptr(k_new), _ptr(v_new), _stream(stream)))
 
 
 def kvs_plan_split(budgets: np.ndarray, head_slot: np.ndarray, Hp: int, cap: float,

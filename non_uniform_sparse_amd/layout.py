@@ -50,10 +50,12 @@ def _nan_fill(t: torch.Tensor) -> None:
 
 
 def build_caches(wl: Workload, head_slot: np.ndarray, device="cuda", poison: bool = True,
-                 seed: int = 1234) -> Tuple[List[Cache], List[RaggedLayout]]:
+                 seed: int = 1234, growth: int = 0) -> Tuple[List[Cache], List[RaggedLayout]]:
     """Allocate and fill the ragged caches of every layer of ``wl``.
 
     head_slot: [L][Hkv] pool positions (group = pos // Hp, slot = pos % Hp).
+    growth: tokens every head may still append; pages and min-max blocks are
+    mapped for n + growth tokens up front, so appends never allocate.
     Returns per-layer device caches (min-max buffers allocated, not built)
     and their host layouts.
     """
@@ -72,7 +74,7 @@ def build_caches(wl: Workload, head_slot: np.ndarray, device="cuda", poison: boo
     for l in range(c.L):
         for h in range(c.Hkv):
             i = hs[l, h] // Hp
-            need[l, :, i] = np.maximum(need[l, :, i], -(-wl.n[:, l, h] // P))
+            need[l, :, i] = np.maximum(need[l, :, i], -(-(wl.n[:, l, h] + growth) // P))
 
     caches: List[Cache] = [None] * c.L
     layouts: List[RaggedLayout] = [None] * c.L
@@ -115,7 +117,7 @@ def build_caches(wl: Workload, head_slot: np.ndarray, device="cuda", poison: boo
                     k = int(need[l, r, i])
                     pt[r, i, :k] = pages(r, i)[:k]
             seq = wl.n[:, l, :].astype(np.int32)
-            runs = (-(-wl.n[:, l, :] // P)).reshape(-1)
+            runs = (-(-(wl.n[:, l, :] + growth) // P)).reshape(-1)
             mb = np.concatenate([[0], np.cumsum(runs)[:-1]]).astype(np.int32).reshape(c.b, c.Hkv)
             mm = torch.empty((max(1, int(runs.sum())), d, 2), dtype=dt, device=device)
             if poison:

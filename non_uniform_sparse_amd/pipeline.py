@@ -69,14 +69,15 @@ class LayerBuffers:
 class DecodeStep:
     def __init__(self, wl: Workload, device="cuda", T: Optional[int] = None,
                  head_slot: Optional[np.ndarray] = None, S: Optional[np.ndarray] = None,
-                 poison: bool = True, microbatches: int = 1):
+                 poison: bool = True, microbatches: int = 1, growth: int = 0):
         c = wl.cfg
         self.wl, self.cfg, self.device = wl, c, device
         if head_slot is None:
             head_slot = (kvs.kvs_cluster_heads(wl.budgets, c.Hp) if c.clustered else
                          np.tile(np.arange(c.Hkv, dtype=np.int32), (c.L, 1)))
         self.head_slot = np.asarray(head_slot, dtype=np.int32)
-        self.caches, self.layouts = build_caches(wl, self.head_slot, device=device, poison=poison)
+        self.caches, self.layouts = build_caches(wl, self.head_slot, device=device, poison=poison,
+                                                 growth=growth)
         for cache in self.caches:
             kvs.kvs_build_minmax(cache)
         dt = torch_dtype(c.dtype)

@@ -187,6 +187,36 @@ class Workload:
                     K[lo:hi, ch] = (K[lo:hi, ch].float() + 3.0).to(K.dtype)
         return K, V
 
+    # ---------------------------------------------------------- decode steps --
+    def step_q(self, t: int, l: int, device="cpu") -> torch.Tensor:
+        """Queries of decode step t of layer l: [b][Hq][d] ~ N(0,1)."""
+        c = self.cfg
+        g = torch.Generator(device=device).manual_seed(_mix(c.seed, 4, t, l))
+        x = torch.randn((c.b, c.Hq, c.d), generator=g, device=device, dtype=torch.float32)
+        return x.to(torch_dtype(c.dtype))
+
+    def step_kv(self, t: int, l: int, device="cpu") -> Tuple[torch.Tensor, torch.Tensor]:
+        """Key and value of the token decoded at step t, for every (request,
+        KV head) of layer l: two [b][Hkv][d] tensors ~ N(0,1)."""
+        c = self.cfg
+        g = torch.Generator(device=device).manual_seed(_mix(c.seed, 5, t, l))
+        x = torch.randn((c.b, c.Hkv, 2, c.d), generator=g, device=device, dtype=torch.float32)
+        x = x.to(torch_dtype(c.dtype))
+        return x[:, :, 0].contiguous(), x[:, :, 1].contiguous()
+
+    def stable_heads(self, unstable_frac: float = 0.25) -> np.ndarray:
+        """[L][Hkv] bool, False for the heads treated as unstable.  Stands in
+        for the offline head classification (the least temporally stable
+        quarter of all heads, FlexiCache summary, Method), which needs real
+        attention data: a seeded choice of round(frac * L * Hkv) of all
+        (layer, head) pairs, so some layers have no unstable head."""
+        c = self.cfg
+        total = c.L * c.Hkv
+        rng = np.random.default_rng(_mix(c.seed, 6))
+        flags = np.ones(total, dtype=bool)
+        flags[rng.permutation(total)[:int(round(unstable_frac * total))]] = False
+        return flags.reshape(c.L, c.Hkv)
+
 
 def make_workload(name: str, **overrides) -> Workload:
     """Draw the host-side structure of a workload.  ``overrides`` may shrink

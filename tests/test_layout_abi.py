@@ -206,3 +206,33 @@ def test_plan_validation():
     with pytest.raises(kvs.KvsError):
         kvs.kvs_cluster_heads(np.full((1, 8), 1.5), 4)
 
+
+
+# ------------------------------------------------ append and head subsets --
+
+def test_append_and_subset_validation():
+    L = _lib()
+    s = _FakeCache().s
+    heads = np.ones(8, dtype=np.uint8)
+    assert L.kvs_append_kv(ctypes.byref(s), None, 0x60000, None) == kvs.KVS_EINVAL
+    assert L.kvs_append_kv(ctypes.byref(s), 0x60008, 0x70000, None) == kvs.KVS_EINVAL  # misaligned
+    assert L.kvs_append_kv(None, 0x60000, 0x70000, None) == kvs.KVS_EINVAL
+    assert L.kvs_score_pages_heads(ctypes.byref(s), 0x60000, None, 0x70000, None) == kvs.KVS_EINVAL
+    s_big = _FakeCache(Hkv=256, Hq=256, Hp=8).s
+    big = np.ones(256, dtype=np.uint8)
+    assert L.kvs_score_pages_heads(ctypes.byref(s_big), 0x60000, big.ctypes.data, 0x70000,
+                                   None) == kvs.KVS_EUNSUPPORTED
+    assert L.kvs_topk_pages_heads(0x10000, 0x20000, 16, 1, 8, 4, 2, None, 0x30000, 0x40000,
+                                  None) == kvs.KVS_EINVAL
+    assert L.kvs_topk_pages_heads(0x10000, 0x20000, 16, 1, 8, 4, 0, heads.ctypes.data, 0x30000,
+                                  0x40000, None) == kvs.KVS_EINVAL
+    assert kvs.last_error()
+
+
+def test_rerank_schedule_matches_oracle():
+    from non_uniform_sparse_amd.steps import heads_due
+    stable = np.array([True, False, True, True, False, True, True, True])
+    for period in (1, 4, 16):
+        for t in range(40):
+            want = [O.rerank_due(t, bool(s), period) for s in stable]
+            assert heads_due(t, stable, period).tolist() == want
