@@ -70,8 +70,13 @@ def algorithmic_bytes(step: DecodeStep, l: int) -> dict:
              + (c.b * c.Hkv * c.topk * 4 * 2 if c.topk else 0)
              + rows * (c.d + 1) * 4 * 2
              + c.b * c.Hq * c.d * 4)
+    maxpg = step.layouts[l].page_table.shape[2]
     return {"kv": kv, "meta": meta, "small": small, "tokens": toks, "units": units,
-            "decode_launch": kv + rows * (c.d + 1) * 4 * 2 + c.b * c.Hq * c.d * (s + 4)}
+            "decode_launch": kv + rows * (c.d + 1) * 4 * 2 + c.b * c.Hq * c.d * (s + 4),
+            # per-call bytes of the other rows
+            "score_launch": meta + c.b * c.Hq * c.d * s + c.b * c.Hkv * maxpg * 4,
+            "topk_launch": int(npg.sum()) * 4 + c.b * c.Hkv * (c.topk or 0) * 4 + c.b * c.Hkv * 4,
+            "minmax_launch": int(n.sum()) * c.d * s + int(npg.sum()) * 2 * c.d * s}
 
 
 def stored_traffic(workload: str):
@@ -378,6 +383,40 @@ def main() -> int:
     # per-step events give the spread either way.
     per_step = sorted(a.elapsed_time(b_) for a, b_ in marks)
     ms = statistics.mean(per_step) if flush is not None else wall_ms / args.steps
+
+    # The other rows of the path, each against the HBM peak: the min-max build
+    # (once per page fill, not in the step) re-run per layer behind a GPU spin,
+    # and the host planner.
+    mm_ms = []
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(int(cycles_per_ms * (2.0 + 0.1 * c.L)))
+        mm_marks = []
+        for l in range(c.L):
+            a, b_ = ev(), ev()
+            a.record(stream)
+            kvs.kvs_build_minmax(step.caches[l], stream)
+            b_.record(stream)
+            mm_marks.append((a, b_))
+    stream.synchronize()
+    mm_ms = [a.elapsed_time(b_) for a, b_ in mm_marks]
+    t_plan = time.perf_counter()
+    for _ in range(20):
+        kvs.kvs_plan_split(wl.budgets, step.head_slot, c.Hp, 0.0, step.T)
+    plan_us = (time.perf_counter() - t_plan) / 20 * 1e6
+
+    def row(ms_list, key):
+        t = statistics.mean(ms_list)
+        by = statistics.mean(a[key] for a in ab)
+        gbps = by / (t * 1e-3) / 1e9
+        return {"us": round(t * 1e3, 2), "bytes": int(by), "GBps": round(gbps, 1),
+                "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    rows = {"a1_minmax_build": dict(row(mm_ms, "minmax_launch"),
+                                    note="once per page fill, not part of the step")}
+    if c.topk:
+        rows["a2_score"] = row(kern["score"], "score_launch")
+        rows["a3_topk"] = dict(row(kern["topk"], "topk_launch"), bound="latency")
+    rows["a4_plan"] = {"us_host": round(plan_us, 1), "note": f"S[{c.L}][{c.G}], host, ahead of time"}
+    rows["a5_a6_decode_combine"] = row(kern["decode_attn"], "decode_launch")
     pct = lambda f: per_step[min(len(per_step) - 1, int(f * len(per_step)))]
     dec_ms = statistics.mean(kern["decode_attn"])
     dec_bytes = statistics.mean(a["decode_launch"] for a in ab)
@@ -410,6 +449,7 @@ def main() -> int:
             "microbatches": len(step.parts),
         },
         "kernels_ms_avg": {k: round(statistics.mean(v), 5) for k, v in kern.items() if v},
+        "rows": rows,
         "roofline": {
             "bound": "hbm",
             "kernel": "kvs_decode_attn (split-K decode + combine)",
