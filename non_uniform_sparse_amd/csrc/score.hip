@@ -25,15 +25,12 @@
 // bounds only to give null pages -inf; pages past a head's end get -inf
 // from a final block-strided fill.  The butterfly order is fixed:
 // deterministic.
-#include <atomic>
-
-#include "kvs_device.h"
+#include "flat_pages.h"
 
 namespace kvs {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kMaxDevices = 64;
+constexpr int kThreads = kFlatThreads;
 
 // Byte selector for v_perm_b32(b, a, sel) with a = (min_c, max_c) and
 // b = (min_c1, max_c1): low half from a (max if q_c >= 0), high half from b.
@@ -44,69 +41,11 @@ __device__ __forceinline__ uint32_t pick_selector(uint32_t q_pair) {
   return lo | (hi << 16);
 }
 
-__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
-
 // Pages of head rh to score: 0 for a head outside the set.
 __device__ __forceinline__ int page_count(const CacheView& c, const HeadMask& heads, int rh) {
   constexpr int P = 16;
   if (!heads.has(rh % c.Hkv)) return 0;
   return (clampi(c.seq_len[rh], 0, P * c.maxpg) + P - 1) / P;
-}
-
-// pre[i] = pages of heads (r, h) with r * Hkv + h < i, for i in [0, b * Hkv];
-// pre[b * Hkv] is the total.  The page counts are first loaded into pre[]
-// with coalesced loads, up to 8 in flight per thread, then summed per
-// contiguous chunk, scanned, and overwritten in place by the prefix.
-__device__ void page_prefix(const CacheView& c, const HeadMask& heads, int* pre, int* part) {
-  const int BH = c.b * c.Hkv;
-  const int tid = threadIdx.x;
-  constexpr int CH = 8;
-  for (int base = 0; base < BH; base += kThreads * CH) {
-    int v[CH];
-#pragma unroll
-    for (int j = 0; j < CH; ++j) v[j] = page_count(c, heads, min(base + j * kThreads + tid, BH - 1));
-#pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const int i = base + j * kThreads + tid;
-      if (i < BH) pre[i] = v[j];
-    }
-  }
-  __syncthreads();
-  const int per = (BH + kThreads - 1) / kThreads;
-  const int lo = min(BH, tid * per), hi = min(BH, lo + per);
-  int s = 0;
-  for (int i = lo; i < hi; ++i) s += pre[i];
-  part[tid] = s;
-  __syncthreads();
-  if (tid < 64) {   // exclusive scan of the 256 partial sums, 4 per lane
-    int v[4], t = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      v[k] = part[4 * tid + k];
-      t += v[k];
-    }
-    int incl = t;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int n = __shfl_up(incl, off, 64);
-      if (tid >= off) incl += n;
-    }
-    int run = incl - t;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      part[4 * tid + k] = run;
-      run += v[k];
-    }
-  }
-  __syncthreads();
-  int run = part[tid];
-  for (int i = lo; i < hi; ++i) {
-    const int n = pre[i];
-    pre[i] = run;
-    run += n;
-  }
-  if (tid == kThreads - 1) pre[BH] = run;
-  __syncthreads();
 }
 
 template <int D, int GQ, typename DT>
@@ -118,26 +57,14 @@ __global__ __launch_bounds__(kThreads) void score_kernel(CacheView c, const uint
   constexpr int RP = PPW * UNROLL;        // pages per round
   extern __shared__ int pre[];
   __shared__ int part[kThreads];
-  page_prefix(c, heads, pre, part);
-
   const int BH = c.b * c.Hkv;
+  page_prefix(BH, [&](int rh) { return page_count(c, heads, rh); }, pre, part);
+
   const int lane = threadIdx.x & 63;
   const int pp = lane / 8, ql = lane % 8;   // page of the step, lane within the page
-  const int64_t W = (int64_t)gridDim.x * (kThreads / 64);
-  const int64_t w = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  const int64_t T = uni(pre[BH]);
-  int t0 = (int)(T * w / W);
-  const int t1 = (int)(T * (w + 1) / W);
-  // head holding flat page t0: the largest hh with pre[hh] <= t0 (non-empty)
-  int hh = 0;
-  {
-    int lo = 0, hi = BH;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) / 2;
-      if (uni(pre[mid]) <= t0) lo = mid; else hi = mid - 1;
-    }
-    hh = lo;
-  }
+  const FlatShare share = flat_share(pre, BH);
+  int t0 = share.t0, hh = share.hh;
+  const int t1 = share.t1;
   const int64_t last = c.num_meta - 1;
   const uint16_t* mmb = reinterpret_cast<const uint16_t*>(c.minmax) + 8 * ql;
 
@@ -226,25 +153,15 @@ __global__ __launch_bounds__(kThreads) void score_kernel(CacheView c, const uint
 }
 
 template <int D, int GQ, typename DT>
+const void* score_symbol() {
+  return reinterpret_cast<const void*>(&score_kernel<D, GQ, DT>);
+}
+
+template <int D, int GQ, typename DT>
 hipError_t launch_v(const CacheView& c, const void* q, float* scores, const HeadMask& heads,
                     hipStream_t s) {
-  // One resident wave per slot: compute units x resident blocks per unit,
-  // found once per device.
-  static std::atomic<int> grid_of[kMaxDevices];
-  int dev = 0;
-  if (hipError_t e = hipGetDevice(&dev)) return e;
-  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  int grid = grid_of[dev].load(std::memory_order_relaxed);
-  if (grid == 0) {
-    int cus = 0, per_cu = 0;
-    if (hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev))
-      return e;
-    if (hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(score_kernel<D, GQ, DT>), kThreads, 0))
-      return e;
-    grid = max(1, cus * max(1, per_cu));
-    grid_of[dev].store(grid, std::memory_order_relaxed);
-  }
+  int grid = 0;   // one resident wave per slot
+  if (hipError_t e = resident_grid<score_symbol<D, GQ, DT>>(&grid)) return e;
   const size_t lds = (size_t)(c.b * c.Hkv + 1) * sizeof(int);
   hipLaunchKernelGGL((score_kernel<D, GQ, DT>), dim3((unsigned)grid), dim3(kThreads), lds, s, c,
                      static_cast<const uint16_t*>(q), scores, heads);
