@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(CacheView c, const uint
                                                          float* __restrict__ scores, HeadMask heads) {
   constexpr int LOADS = D / 32;           // 16-byte loads per lane per page
   constexpr int PPW = 8;                  // pages per step (8 lanes each)
-  constexpr int UNROLL = 16 / LOADS;      // steps per round: 64 data registers
+  constexpr int UNROLL = 8 / LOADS > 0 ? 8 / LOADS : 1;   // steps per round: 32 data registers
   constexpr int RP = PPW * UNROLL;        // pages per round
   extern __shared__ int pre[];
   __shared__ int part[kThreads];

@@ -109,6 +109,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     // has the same digit, it is the digit, with no histogram (and no atomic
     // contention on one bin).
     int dmin = 256, dmax = -1;
+#pragma unroll 4
     for (int p = tid; p < npg; p += kThreads) {
       const uint32_t k = keys[p];
       if ((k & mask) == prefix) {
@@ -125,6 +126,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     }
     hist[tid] = 0;   // kThreads == 256 bins
     __syncthreads();
+#pragma unroll 4
     for (int p = tid; p < npg; p += kThreads) {
       const uint32_t k = keys[p];
       if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1);
