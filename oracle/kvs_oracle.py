@@ -42,6 +42,9 @@ __all__ = [
     "rerank_due",
     "layer_scoring_needed",
     "decode_head_steps",
+    "chunk_quota",
+    "top_tokens",
+    "prefill_head",
 ]
 
 
@@ -383,3 +386,50 @@ def decode_head_steps(q_steps: np.ndarray, K0: np.ndarray, V0: np.ndarray,
         outs.append(decode_head(q_steps[t], Kc, Vc, sel, P, scale))
         sels.append(np.array(sel, dtype=np.int64))
     return np.stack(outs), sels
+
+
+# ---------------------------------------------------------------------------
+# Budget Reservation in chunked prefill -- Tangram review, 3.1: as each
+# prefill chunk's K/V is computed, every head keeps its top tokens by a score
+# s, Top(ceil(B N), s) in all, so the compressed footprint is fixed when the
+# request is scheduled and nothing is reclaimed later.
+# ---------------------------------------------------------------------------
+
+def chunk_quota(budget: float, start: int, end: int) -> int:
+    """Tokens a head keeps from the chunk covering positions [start, end) of
+    its prompt.  Reading: the cumulative kept count after position x is
+    ceil(B x) (retained_count), so a chunk keeps ceil(B end) - ceil(B start);
+    over all chunks of an N-token prompt this telescopes to ceil(B N), and it
+    never exceeds the chunk's length since B <= 1."""
+    if not 0 <= start <= end:
+        raise ValueError("0 <= start <= end required")
+    before = 0 if start == 0 else retained_count(budget, start)
+    return (0 if end == 0 else retained_count(budget, end)) - before
+
+
+def top_tokens(scores: Sequence[float], k: int) -> np.ndarray:
+    """Positions of the k largest scores, equal scores to the lower position,
+    returned in ascending position (the order in which they are kept)."""
+    if k < 0:
+        raise ValueError("k must be >= 0")
+    s = [float(x) for x in scores]
+    ranked = sorted(range(len(s)), key=lambda t: (-s[t], t))
+    return np.array(sorted(ranked[:min(k, len(s))]), dtype=np.int64)
+
+
+def prefill_head(K_chunks: Sequence[np.ndarray], V_chunks: Sequence[np.ndarray],
+                 s_chunks: Sequence[np.ndarray], budget: float):
+    """The keys and values one head holds after a chunked prefill: for each
+    chunk in order, its top chunk_quota tokens by score, in position order,
+    appended after those kept from earlier chunks.  Returns (K, V) [n][d]."""
+    keptK, keptV, start = [], [], 0
+    for Kc, Vc, sc in zip(K_chunks, V_chunks, s_chunks):
+        end = start + len(sc)
+        idx = top_tokens(sc, chunk_quota(budget, start, end))
+        keptK.append(np.asarray(Kc, dtype=np.float64)[idx])
+        keptV.append(np.asarray(Vc, dtype=np.float64)[idx])
+        start = end
+    d = np.asarray(K_chunks[0]).shape[1]
+    K = np.concatenate(keptK) if keptK else np.zeros((0, d))
+    V = np.concatenate(keptV) if keptV else np.zeros((0, d))
+    return K, V

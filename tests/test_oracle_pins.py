@@ -462,3 +462,43 @@ def test_decode_steps_stable_head_keeps_stale_pages():
     # an unstable head sees the new high-key pages instead
     _, sels_u = O.decode_head_steps(q, K0, V0, kn, vn, False, K, P, 1.0, 16)
     assert sels_u[-1].tolist() != first
+
+
+# ------------------------------------------------ budget reservation -------
+
+def test_chunk_budget_golden():
+    g = GOLD["chunk_budget"]
+    C, N, B = g["chunk"], g["N"], g["budget"]
+    starts = list(range(0, N, C))
+    assert [O.chunk_quota(B, a, min(N, a + C)) for a in starts] == g["quotas"]
+    d = 1
+    Ks = [np.arange(a, min(N, a + C), dtype=float)[:, None] for a in starts]   # K = global position
+    Vs = [-k for k in Ks]
+    K, V = O.prefill_head(Ks, Vs, [np.array(s) for s in g["scores"]], B)
+    assert K[:, 0].tolist() == g["kept_global"] and V[:, 0].tolist() == [-x for x in g["kept_global"]]
+
+
+@pytest.mark.parametrize("B,N,C", [(0.3, 1000, 64), (1.0, 77, 16), (0.01, 5000, 512),
+                                   (0.577, 32768, 2048), (1 / 3, 99, 7)])
+def test_chunk_quotas_telescope_to_the_budget(B, N, C):
+    """Summed over the chunks, the quotas are ceil(B N), each at most the
+    chunk's length (the footprint is fixed when the request is scheduled)."""
+    q = [O.chunk_quota(B, a, min(N, a + C)) for a in range(0, N, C)]
+    assert sum(q) == O.retained_count(B, N)
+    assert all(0 <= x <= min(C, N - a) for x, a in zip(q, range(0, N, C)))
+
+
+def test_prefill_one_chunk_full_budget_and_brute_force():
+    """B = 1 keeps every token; on tiny chunks the selection equals the brute
+    force over all subsets of the quota's size (maximal score sum, then the
+    lexicographically smallest positions among equal sums)."""
+    import itertools
+    rng = np.random.default_rng(2)
+    K = rng.normal(size=(12, 3)); V = rng.normal(size=(12, 3))
+    s = rng.integers(0, 4, size=12).astype(float)          # many ties
+    Kf, Vf = O.prefill_head([K], [V], [s], 1.0)
+    assert np.array_equal(Kf, K) and np.array_equal(Vf, V)
+    for k in range(0, 6):
+        best = max(itertools.combinations(range(12), k),
+                   key=lambda c: (sum(s[list(c)]), [-t for t in c]))
+        assert O.top_tokens(s, k).tolist() == list(best)
