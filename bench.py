@@ -187,6 +187,51 @@ def rerank_reuse_report(configs, period: int = 16, unstable_frac: float = 0.25,
     return out
 
 
+def prefill_report(configs, chunk: int = 2048) -> dict:
+    """Chunked prefill under Budget Reservation (Tangram review, 3.1): every
+    chunk of every layer, selection + compaction + page bounds in one
+    kvs_prefill_chunk launch each.  Each launch is timed with events behind a
+    short GPU spin (its inputs are generated before and are not timed).
+    Bytes: the chunk's scores, the kept tokens' K/V read and written, and
+    the bounds of the pages written."""
+    from non_uniform_sparse_amd.prefill import ChunkedPrefill
+    out = {}
+    stream = torch.cuda.current_stream()
+    rate = sleep_rate(stream)
+    for name in configs:
+        ov = {"L": 8} if name == "gemma3_mixed" else {}
+        wl = make_workload(name, **ov)
+        c = wl.cfg
+        pf = ChunkedPrefill(wl, chunk, device="cuda")
+        total_ms, total_bytes, kept, launches = 0.0, 0, 0, 0
+        for k in range(pf.chunks):
+            for l in range(c.L):
+                inp = pf.inputs(l, k)
+                q_np = pf.quota(l, k)
+                q = torch.from_numpy(q_np).to("cuda")
+                torch.cuda._sleep(int(rate * 0.3))
+                a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                pf.run_chunk(l, k, inputs=inp, quota=q)
+                b_.record()
+                b_.synchronize()
+                total_ms += a.elapsed_time(b_)
+                qs = int(q_np.sum())
+                pages = int(np.ceil(q_np / c.P).sum()) + c.b * c.Hkv   # bound on pages touched
+                total_bytes += (c.b * c.Hkv * chunk * 4 + qs * 2 * c.d * 2 * 2
+                                + pages * 2 * c.d * 2)
+                kept += qs
+                launches += 1
+        gbps = total_bytes / (total_ms * 1e-3) / 1e9
+        out[name] = {"layers": c.L, "requests": c.b, "chunk": chunk, "launches": launches,
+                     "tokens_in": int(wl.contexts.sum()) * c.L * c.Hkv, "tokens_kept": kept,
+                     "us_per_launch": round(total_ms / launches * 1e3, 2),
+                     "GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+        del pf
+        torch.cuda.empty_cache()
+    return out
+
+
 def skew_report(configs, launches: int = 20) -> dict:
     """Per-workgroup duration skew of the split-K decode kernel, max / mean
     over the workgroups of one launch, median over launches, per layer; with
@@ -256,6 +301,9 @@ def main() -> int:
                     help="request micro-batches, each on a stream of its own in the step graph "
                          "(0: one below 4 layers, else min(3, requests))")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill", nargs="*", default=None, metavar="CONFIG",
+                    help="time the chunked prefill under Budget Reservation (default configs: "
+                         "llama8b_ragged, gemma3_mixed at 8 layers) and print that record")
     ap.add_argument("--rerank-reuse", nargs="*", default=None, metavar="CONFIG",
                     help="time decoding over steps with stability-aware reranking against "
                          "reranking every step (default configs: flexicache_topk, gemma3_mixed "
@@ -275,6 +323,10 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.prefill is not None:
+        print(json.dumps({"prefill": prefill_report(args.prefill or ["llama8b_ragged",
+                                                                     "gemma3_mixed"])}))
+        return 0
     if args.rerank_reuse is not None:
         print(json.dumps({"rerank_reuse": rerank_reuse_report(
             args.rerank_reuse or ["flexicache_topk", "gemma3_mixed"])}))

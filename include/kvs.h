@@ -184,6 +184,32 @@ int kvs_topk_pages_heads(const float* scores, const int32_t* seq_len, int32_t P,
 int kvs_append_kv(const kvs_paged_kv* cache, const void* k_new, const void* v_new, void* stream);
 
 /*
+ * One chunk of a chunked prefill under Budget Reservation [T 3.1: as each
+ * chunk's K/V is computed, every head keeps its top tokens by a score, so the
+ * compressed footprint is fixed at scheduling and nothing is reclaimed]:
+ * for every (r, h) with n = seq_len[r][h], keep the q = quota[r][h] tokens
+ * of the chunk with the largest score (equal scores to the lower position),
+ * write them in position order to positions n .. n+q-1 of the head's slot
+ * in its group's pages [T 3.2], update the min-max bounds of every page they
+ * land in [F Key observations, assumption 2] (merged with the bounds the
+ * first page already held), and set seq_len[r][h] = n + q.  q is clamped to
+ * [0, min(C, P*max_group_pages - n)].  The quota is the caller's: under the
+ * reading used here, chunk [a, e) of an N-token prompt keeps
+ * ceil(B e) - ceil(B a) tokens, ceil(B N) in all.
+ *   k_chunk, v_chunk  device, [b][Hkv][C][d] dtype, 16-byte aligned.
+ *   scores            device, [b][Hkv][C] fp32 (integer keys from the fp32
+ *                     bits, as in kvs_topk_pages).
+ *   quota             device, [b][Hkv] int32.
+ *   C                 chunk length, 1 <= C <= 8192.
+ * The pages for positions n .. n+q-1 must be mapped and the head must own
+ * blocks meta_base[r][h] + p for them (the reservation).  A token whose page
+ * entry is null is not written; a head whose head_slot is out of range is
+ * left as it is.
+ */
+int kvs_prefill_chunk(const kvs_paged_kv* cache, const void* k_chunk, const void* v_chunk,
+                      const float* scores, const int32_t* quota, int32_t C, void* stream);
+
+/*
  * Ahead-of-time workload split map [T 3.3], host only.
  * Per layer l: weight w_h = round(min(B[l][h], cap) * 2^20) (cap <= 0: no
  * cap), group load phi_i = sum of w_h over the heads with head_slot/Hp == i,

@@ -193,6 +193,25 @@ extern "C" int kvs_topk_pages_heads(const float* scores, const int32_t* seq_len,
   return topk_impl(scores, seq_len, P, b, Hkv, max_pages, K, m, sel, sel_count, stream, fn);
 }
 
+extern "C" int kvs_prefill_chunk(const kvs_paged_kv* cache, const void* k_chunk,
+                                 const void* v_chunk, const float* scores, const int32_t* quota,
+                                 int32_t C, void* stream) {
+  clear_error();
+  static const char* fn = "kvs_prefill_chunk";
+  CacheView c;
+  if (int rc = check_cache(cache, true, fn, &c)) return rc;
+  if (!k_chunk || !v_chunk || !scores || !quota)
+    return set_error(KVS_EINVAL, "%s: null chunk, scores or quota", fn);
+  if (!aligned16(k_chunk) || !aligned16(v_chunk))
+    return set_error(KVS_EINVAL, "%s: k_chunk and v_chunk must be 16-byte aligned", fn);
+  if (C < 1 || C > kMaxChunk)
+    return set_error(KVS_EINVAL, "%s: chunk length %d not in [1, %d]", fn, C, kMaxChunk);
+  if ((int64_t)c.b * c.Hkv > 0x7fffffff) return set_error(KVS_EINVAL, "%s: b*Hkv too large", fn);
+  if (hipError_t e = launch_prefill(c, k_chunk, v_chunk, scores, quota, C, (hipStream_t)stream))
+    return hip_error(e, fn);
+  return KVS_OK;
+}
+
 extern "C" int kvs_append_kv(const kvs_paged_kv* cache, const void* k_new, const void* v_new,
                              void* stream) {
   clear_error();

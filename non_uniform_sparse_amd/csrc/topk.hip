@@ -1,202 +1,35 @@
 // Per-KV-head top-K page selection (FlexiCache summary, Core method: each
 // head attends only its K best pages).  One 256-thread workgroup per
-// (request, head).  Scores become order-preserving 32-bit keys held in LDS;
-// a most-significant-digit radix select (4 passes of 8 bits) finds the K-th
-// largest key tau.  A pass whose candidate keys (those matching the digits
-// chosen so far) all share one digit takes it directly; otherwise it builds a
-// 256-bin LDS histogram of the candidates, one wave owns the bins (4 per
-// lane), a suffix scan over its lanes gives the count above each lane's bins
-// and the one lane whose bins straddle the K-th key publishes the digit.
-// Pages with key > tau are kept, and among pages with key == tau the lowest
-// page indices fill the remaining places.  To place them, each thread owns
-// one contiguous run of pages and counts its keys above and equal to tau;
-// one block-wide exclusive scan of the two counts (packed in one int) gives
-// each thread its first output position and the ties taken before it, and
-// the thread writes its kept pages in page order.  Integer work only, so the
-// result is deterministic.
-#include "kvs_device.h"
+// (request, head) runs the block selection of radix_select.h over the
+// head's page scores and writes the kept pages in ascending page order;
+// entries past the kept count are -1.  A head outside the given set keeps
+// the selection it holds.  Integer work only, so the result is
+// deterministic.
+#include "radix_select.h"
 
 namespace kvs {
 namespace {
 
-// Larger float -> larger key; -0 and +0 map to the same key.
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
-
-// Block-wide exclusive prefix sum of one int per thread, in thread order.
-__device__ __forceinline__ int block_exclusive_scan(int v, int* red) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int t = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += t;
-  }
-  if (lane == 63) red[wid] = incl;
-  __syncthreads();
-  int before = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) before += w < wid ? red[w] : 0;
-  __syncthreads();
-  return before + incl - v;
-}
-
-// Block-wide min and max of one int per thread (every thread gets both).
-__device__ __forceinline__ void block_minmax(int lo, int hi, int* red, int* out_lo, int* out_hi) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  lo = -(int)group_max<64>(-(float)lo);
-  hi = (int)group_max<64>((float)hi);
-  if (lane == 0) {
-    red[wid] = lo;
-    red[kWaves + wid] = hi;
-  }
-  __syncthreads();
-  int a = red[0], b = red[kWaves];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) {
-    a = min(a, red[w]);
-    b = max(b, red[kWaves + w]);
-  }
-  __syncthreads();
-  *out_lo = a;
-  *out_hi = b;
-}
-
-__global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ scores,
-                                                        const int32_t* __restrict__ seq_len, int P,
-                                                        int max_pages, int K, int Hkv,
-                                                        HeadMask heads,
-                                                        int32_t* __restrict__ sel,
-                                                        int32_t* __restrict__ sel_count) {
+__global__ __launch_bounds__(kSelThreads) void topk_kernel(const float* __restrict__ scores,
+                                                           const int32_t* __restrict__ seq_len,
+                                                           int P, int max_pages, int K, int Hkv,
+                                                           HeadMask heads,
+                                                           int32_t* __restrict__ sel,
+                                                           int32_t* __restrict__ sel_count) {
   extern __shared__ uint32_t keys[];   // [max_pages]
-  __shared__ int hist[256];
-  __shared__ int red[2 * kWaves];
-  __shared__ int s_digit, s_need;
+  __shared__ SelectShared sh;
   const int rh = blockIdx.x;
   if (!heads.has(rh % Hkv)) return;   // a head outside the set keeps its selection
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x;
   const int n = clampi(seq_len[rh], 0, P * max_pages);
   const int npg = (n + P - 1) / P;
   const int keep = min(K, npg);
-  const float* row = scores + (int64_t)rh * max_pages;
   int32_t* out = sel + (int64_t)rh * K;
 
-  // All of a thread's loads are issued before the first store, so a long
-  // row costs one memory round trip per 4096 pages, not one per 256.
-  constexpr int CH = 16;
-  for (int base = 0; base < npg; base += kThreads * CH) {
-    float v[CH];
-#pragma unroll
-    for (int j = 0; j < CH; ++j) v[j] = row[min(base + j * kThreads + tid, npg - 1)];
-#pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const int p = base + j * kThreads + tid;
-      if (p < npg) keys[p] = order_key(v[j]);
-    }
-  }
-  __syncthreads();
-
-  uint32_t prefix = 0, mask = 0;
-  int need = keep;   // keys equal to the final prefix still to take
-  for (int shift = 24; shift >= 0 && keep > 0; shift -= 8) {
-    // Scores of one head often share their top bits: if every candidate key
-    // has the same digit, it is the digit, with no histogram (and no atomic
-    // contention on one bin).
-    int dmin = 256, dmax = -1;
-#pragma unroll 4
-    for (int p = tid; p < npg; p += kThreads) {
-      const uint32_t k = keys[p];
-      if ((k & mask) == prefix) {
-        const int dg = (int)((k >> shift) & 255u);
-        dmin = min(dmin, dg);
-        dmax = max(dmax, dg);
-      }
-    }
-    block_minmax(dmin, dmax, red, &dmin, &dmax);
-    if (dmin == dmax) {
-      prefix |= (uint32_t)dmin << shift;
-      mask |= 255u << shift;
-      continue;
-    }
-    hist[tid] = 0;   // kThreads == 256 bins
-    __syncthreads();
-#pragma unroll 4
-    for (int p = tid; p < npg; p += kThreads) {
-      const uint32_t k = keys[p];
-      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1);
-    }
-    __syncthreads();
-    if (wid == 0) {
-      int hb[4], mine = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        hb[i] = hist[4 * lane + i];
-        mine += hb[i];
-      }
-      // inclusive suffix sum over lanes (lane 63 holds the largest digits)
-      int incl = mine;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_down(incl, off, 64);
-        if (lane + off < 64) incl += t;
-      }
-      int acc = incl - mine;   // keys in bins above this lane's
-      int found = -1, left = 0;
-#pragma unroll
-      for (int i = 3; i >= 0; --i) {
-        if (found < 0 && acc < need && need <= acc + hb[i]) {
-          found = 4 * lane + i;
-          left = need - acc;
-        }
-        acc += hb[i];
-      }
-      if (found >= 0) {   // exactly one lane
-        s_digit = found;
-        s_need = left;
-      }
-    }
-    __syncthreads();
-    prefix |= (uint32_t)s_digit << shift;
-    need = s_need;
-    mask |= 255u << shift;
-    __syncthreads();
-  }
-  const uint32_t tau = prefix;
-  const int ties = need;
-
-  // Thread tid owns pages [p_lo, p_hi): count keys above and equal to tau
-  // (each count < 2^14 since max_pages <= 8192), scan, then place.
-  if (keep > 0) {
-    const int per = (npg + kThreads - 1) / kThreads;
-    const int p_lo = min(npg, tid * per), p_hi = min(npg, p_lo + per);
-    int n_gt = 0, n_eq = 0;
-    for (int p = p_lo; p < p_hi; ++p) {
-      const uint32_t k = keys[p];
-      n_gt += k > tau;
-      n_eq += k == tau;
-    }
-    const int before = block_exclusive_scan((n_gt << 16) | n_eq, red);
-    const int gt_before = before >> 16, eq_before = before & 0xffff;
-    int pos = gt_before + min(eq_before, ties);
-    int eq_seen = eq_before;
-    for (int p = p_lo; p < p_hi; ++p) {
-      const uint32_t k = keys[p];
-      const bool eq = k == tau;
-      const bool take = k > tau || (eq && eq_seen < ties);
-      eq_seen += eq;
-      if (take) {
-        if (pos < keep) out[pos] = p;
-        ++pos;
-      }
-    }
-  }
-  for (int k = keep + tid; k < K; k += kThreads) out[k] = -1;
+  load_keys(scores + (int64_t)rh * max_pages, npg, keys);
+  const Threshold th = kth_largest(keys, npg, keep, sh);
+  place_kept(keys, npg, keep, th, sh, [&](int pos, int p) { out[pos] = p; });
+  for (int k = keep + tid; k < K; k += kSelThreads) out[k] = -1;
   if (tid == 0) sel_count[rh] = keep;
 }
 
@@ -206,8 +39,8 @@ hipError_t launch_topk(const float* scores, const int32_t* seq_len, int P, int b
                        int max_pages, int K, const HeadMask& heads, int32_t* sel,
                        int32_t* sel_count, hipStream_t s) {
   const size_t lds = (size_t)max_pages * sizeof(uint32_t);
-  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)(b * Hkv)), dim3(kThreads), lds, s, scores, seq_len, P,
-                     max_pages, K, Hkv, heads, sel, sel_count);
+  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)(b * Hkv)), dim3(kSelThreads), lds, s, scores,
+                     seq_len, P, max_pages, K, Hkv, heads, sel, sel_count);
   return hipGetLastError();
 }
 

@@ -25,7 +25,8 @@ KVS_F16, KVS_BF16 = 0, 1
 # Every symbol include/kvs.h declares.
 EXPORTS = (
     "kvs_build_minmax", "kvs_score_pages", "kvs_score_pages_heads", "kvs_topk_pages",
-    "kvs_topk_pages_heads", "kvs_append_kv", "kvs_plan_split", "kvs_decode_attn",
+    "kvs_topk_pages_heads", "kvs_append_kv", "kvs_prefill_chunk", "kvs_plan_split",
+    "kvs_decode_attn",
     "kvs_decode_workspace_bytes", "kvs_decode_concurrency", "kvs_cluster_heads",
     "kvs_last_error",
 )
@@ -80,6 +81,7 @@ def lib() -> ctypes.CDLL:
         L.kvs_topk_pages.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
         L.kvs_topk_pages_heads.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
         L.kvs_append_kv.argtypes = [pkv, vp, vp, vp]
+        L.kvs_prefill_chunk.argtypes = [pkv, vp, vp, vp, vp, i32, vp]
         L.kvs_plan_split.argtypes = [vp, vp, i32, i32, i32, f64, i32, vp]
         L.kvs_decode_attn.argtypes = [pkv, vp, vp, vp, i32, vp, f32, vp, ctypes.c_size_t, vp, vp]
         L.kvs_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, vp, i32]
@@ -219,6 +221,21 @@ def kvs_append_kv(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor, stream
     _need(k_new, "k_new", (s.b, s.Hkv, s.d), cache.kv.dtype, dev)
     _need(v_new, "v_new", (s.b, s.Hkv, s.d), cache.kv.dtype, dev)
     _check(lib().kvs_append_kv(ctypes.byref(s), _ptr(k_new), _ptr(v_new), _stream(stream)))
+
+
+def kvs_prefill_chunk(cache: Cache, k_chunk: torch.Tensor, v_chunk: torch.Tensor,
+                      scores: torch.Tensor, quota: torch.Tensor, stream=None) -> None:
+    """Keep each head's quota best tokens of a prefill chunk, append them to
+    its pages, update their bounds and advance seq_len on the device."""
+    s = cache.struct()
+    dev = cache.kv.device
+    C = k_chunk.shape[2]
+    _need(k_chunk, "k_chunk", (s.b, s.Hkv, C, s.d), cache.kv.dtype, dev)
+    _need(v_chunk, "v_chunk", (s.b, s.Hkv, C, s.d), cache.kv.dtype, dev)
+    _need(scores, "scores", (s.b, s.Hkv, C), torch.float32, dev)
+    _need(quota, "quota", (s.b, s.Hkv), torch.int32, dev)
+    _check(lib().kvs_prefill_chunk(ctypes.byref(s), _ptr(k_chunk), _ptr(v_chunk), _ptr(scores),
+                                   _ptr(quota), int(C), _stream(stream)))
 
 
 def kvs_plan_split(budgets: np.ndarray, head_slot: np.ndarray, Hp: int, cap: float,
