@@ -200,14 +200,25 @@ int kvs_append_kv(const kvs_paged_kv* cache, const void* k_new, const void* v_ne
  *   scores            device, [b][Hkv][C] fp32 (integer keys from the fp32
  *                     bits, as in kvs_topk_pages).
  *   quota             device, [b][Hkv] int32.
- *   C                 chunk length, 1 <= C <= 8192.
+ *   C                 chunk length, 1 <= C <= 8192.  Positions past a
+ *                     request's prompt must carry -inf scores; the quota
+ *                     never exceeds the number of the others.
+ *   workspace         device scratch of at least
+ *                     kvs_prefill_workspace_bytes(b, Hkv, C) bytes, 256-byte
+ *                     aligned; contents on entry do not matter.
+ *   b*Hkv <= 65535 (KVS_EUNSUPPORTED otherwise).
  * The pages for positions n .. n+q-1 must be mapped and the head must own
  * blocks meta_base[r][h] + p for them (the reservation).  A token whose page
  * entry is null is not written; a head whose head_slot is out of range is
  * left as it is.
  */
 int kvs_prefill_chunk(const kvs_paged_kv* cache, const void* k_chunk, const void* v_chunk,
-                      const float* scores, const int32_t* quota, int32_t C, void* stream);
+                      const float* scores, const int32_t* quota, int32_t C, void* workspace,
+                      size_t ws_bytes, void* stream);
+
+/* Bytes of workspace kvs_prefill_chunk needs (per head: its length before
+ * the chunk, its quota and the kept positions).  0 on bad arguments. */
+size_t kvs_prefill_workspace_bytes(int32_t b, int32_t Hkv, int32_t C);
 
 /*
  * Ahead-of-time workload split map [T 3.3], host only.

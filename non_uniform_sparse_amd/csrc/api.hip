@@ -193,9 +193,14 @@ extern "C" int kvs_topk_pages_heads(const float* scores, const int32_t* seq_len,
   return topk_impl(scores, seq_len, P, b, Hkv, max_pages, K, m, sel, sel_count, stream, fn);
 }
 
+extern "C" size_t kvs_prefill_workspace_bytes(int32_t b, int32_t Hkv, int32_t C) {
+  if (b < 1 || Hkv < 1 || C < 1 || C > kMaxChunk) return 0;
+  return prefill_workspace_bytes(b, Hkv, C);
+}
+
 extern "C" int kvs_prefill_chunk(const kvs_paged_kv* cache, const void* k_chunk,
                                  const void* v_chunk, const float* scores, const int32_t* quota,
-                                 int32_t C, void* stream) {
+                                 int32_t C, void* workspace, size_t ws_bytes, void* stream) {
   clear_error();
   static const char* fn = "kvs_prefill_chunk";
   CacheView c;
@@ -206,8 +211,14 @@ extern "C" int kvs_prefill_chunk(const kvs_paged_kv* cache, const void* k_chunk,
     return set_error(KVS_EINVAL, "%s: k_chunk and v_chunk must be 16-byte aligned", fn);
   if (C < 1 || C > kMaxChunk)
     return set_error(KVS_EINVAL, "%s: chunk length %d not in [1, %d]", fn, C, kMaxChunk);
-  if ((int64_t)c.b * c.Hkv > 0x7fffffff) return set_error(KVS_EINVAL, "%s: b*Hkv too large", fn);
-  if (hipError_t e = launch_prefill(c, k_chunk, v_chunk, scores, quota, C, (hipStream_t)stream))
+  if ((int64_t)c.b * c.Hkv > 65535) return set_error(KVS_EUNSUPPORTED, "%s: b*Hkv > 65535", fn);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return set_error(KVS_EINVAL, "%s: workspace must be non-null and 256-byte aligned", fn);
+  const size_t need = prefill_workspace_bytes(c.b, c.Hkv, C);
+  if (ws_bytes < need)
+    return set_error(KVS_ENOSPC, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+  if (hipError_t e = launch_prefill(c, k_chunk, v_chunk, scores, quota, C, workspace,
+                                    (hipStream_t)stream))
     return hip_error(e, fn);
   return KVS_OK;
 }

@@ -17,7 +17,7 @@ constexpr int kMaxTopkPages = 8192;
 constexpr int kMaxK = 1024;
 constexpr int kMaxSplitsPerRequest = 65536;
 constexpr int kMaxScoreHeads = 16383;
-constexpr int kMaxChunk = 8192;          // prefill chunk length (LDS: 6 bytes per token)   // b * Hkv: page-count prefix held in 64 KB of LDS
+constexpr int kMaxChunk = 8192;          // prefill chunk length (16-bit kept positions)   // b * Hkv: page-count prefix held in 64 KB of LDS
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Records a message for kvs_last_error() and returns `code`.
@@ -71,7 +71,9 @@ hipError_t launch_topk(const float* scores, const int32_t* seq_len, int P, int b
                        int32_t* sel_count, hipStream_t s);
 hipError_t launch_append(const CacheView& c, const void* k_new, const void* v_new, hipStream_t s);
 hipError_t launch_prefill(const CacheView& c, const void* k_chunk, const void* v_chunk,
-                          const float* scores, const int32_t* quota, int C, hipStream_t s);
+                          const float* scores, const int32_t* quota, int C, void* ws,
+                          hipStream_t s);
+size_t prefill_workspace_bytes(int b, int Hkv, int C);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s);
 // Resident decode workgroups per compute unit for a kernel variant.

@@ -25,7 +25,8 @@ KVS_F16, KVS_BF16 = 0, 1
 # Every symbol include/kvs.h declares.
 EXPORTS = (
     "kvs_build_minmax", "kvs_score_pages", "kvs_score_pages_heads", "kvs_topk_pages",
-    "kvs_topk_pages_heads", "kvs_append_kv", "kvs_prefill_chunk", "kvs_plan_split",
+    "kvs_topk_pages_heads", "kvs_append_kv", "kvs_prefill_chunk", "kvs_prefill_workspace_bytes",
+    "kvs_plan_split",
     "kvs_decode_attn",
     "kvs_decode_workspace_bytes", "kvs_decode_concurrency", "kvs_cluster_heads",
     "kvs_last_error",
@@ -81,7 +82,9 @@ def lib() -> ctypes.CDLL:
         L.kvs_topk_pages.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
         L.kvs_topk_pages_heads.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
         L.kvs_append_kv.argtypes = [pkv, vp, vp, vp]
-        L.kvs_prefill_chunk.argtypes = [pkv, vp, vp, vp, vp, i32, vp]
+        L.kvs_prefill_chunk.argtypes = [pkv, vp, vp, vp, vp, i32, vp, ctypes.c_size_t, vp]
+        L.kvs_prefill_workspace_bytes.argtypes = [i32, i32, i32]
+        L.kvs_prefill_workspace_bytes.restype = ctypes.c_size_t
         L.kvs_plan_split.argtypes = [vp, vp, i32, i32, i32, f64, i32, vp]
         L.kvs_decode_attn.argtypes = [pkv, vp, vp, vp, i32, vp, f32, vp, ctypes.c_size_t, vp, vp]
         L.kvs_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, vp, i32]
@@ -93,7 +96,8 @@ def lib() -> ctypes.CDLL:
             L.kvs_decode_stamps_offset.argtypes = [i32, i32, i32, i32, vp, i32]
             L.kvs_decode_stamps_offset.restype = ctypes.c_size_t
         for name in EXPORTS:
-            if name not in ("kvs_decode_workspace_bytes", "kvs_last_error"):
+            if name not in ("kvs_decode_workspace_bytes", "kvs_prefill_workspace_bytes",
+                            "kvs_last_error"):
                 getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -223,8 +227,13 @@ def kvs_append_kv(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor, stream
     _check(lib().kvs_append_kv(ctypes.byref(s), _ptr(k_new), _ptr(v_new), _stream(stream)))
 
 
+def kvs_prefill_workspace_bytes(b: int, Hkv: int, C: int) -> int:
+    return int(lib().kvs_prefill_workspace_bytes(b, Hkv, C))
+
+
 def kvs_prefill_chunk(cache: Cache, k_chunk: torch.Tensor, v_chunk: torch.Tensor,
-                      scores: torch.Tensor, quota: torch.Tensor, stream=None) -> None:
+                      scores: torch.Tensor, quota: torch.Tensor, workspace: torch.Tensor,
+                      stream=None) -> None:
     """Keep each head's quota best tokens of a prefill chunk, append them to
     its pages, update their bounds and advance seq_len on the device."""
     s = cache.struct()
@@ -234,8 +243,11 @@ def kvs_prefill_chunk(cache: Cache, k_chunk: torch.Tensor, v_chunk: torch.Tensor
     _need(v_chunk, "v_chunk", (s.b, s.Hkv, C, s.d), cache.kv.dtype, dev)
     _need(scores, "scores", (s.b, s.Hkv, C), torch.float32, dev)
     _need(quota, "quota", (s.b, s.Hkv), torch.int32, dev)
+    if not workspace.is_contiguous() or workspace.device != dev:
+        raise ValueError("workspace must be a contiguous tensor on the cache's device")
+    nbytes = workspace.numel() * workspace.element_size()
     _check(lib().kvs_prefill_chunk(ctypes.byref(s), _ptr(k_chunk), _ptr(v_chunk), _ptr(scores),
-                                   _ptr(quota), int(C), _stream(stream)))
+                                   _ptr(quota), int(C), _ptr(workspace), nbytes, _stream(stream)))
 
 
 def kvs_plan_split(budgets: np.ndarray, head_slot: np.ndarray, Hp: int, cap: float,

@@ -57,6 +57,8 @@ class ChunkedPrefill:
         # the reservation: every head's pages and bounds blocks for n = ceil(B N)
         self.ds = DecodeStep(wl, device=device, poison=True)
         self.chunks = int(-(-int(wl.contexts.max()) // chunk))
+        self.workspace = torch.empty(kvs.kvs_prefill_workspace_bytes(c.b, c.Hkv, chunk),
+                                     dtype=torch.uint8, device=device)
         self.reset()
 
     def reset(self) -> None:
@@ -93,4 +95,4 @@ class ChunkedPrefill:
     def run_chunk(self, l: int, k: int, inputs=None, quota=None, stream=None) -> None:
         kc, vc, s = inputs if inputs is not None else self.inputs(l, k)
         q = quota if quota is not None else torch.from_numpy(self.quota(l, k)).to(self.device)
-        kvs.kvs_prefill_chunk(self.ds.caches[l], kc, vc, s, q, stream)
+        kvs.kvs_prefill_chunk(self.ds.caches[l], kc, vc, s, q, self.workspace, stream)
