@@ -45,6 +45,8 @@ __all__ = [
     "chunk_quota",
     "top_tokens",
     "prefill_head",
+    "rerank_promotion",
+    "decode_head_rerank",
 ]
 
 
@@ -433,3 +435,39 @@ def prefill_head(K_chunks: Sequence[np.ndarray], V_chunks: Sequence[np.ndarray],
     K = np.concatenate(keptK) if keptK else np.zeros((0, d))
     V = np.concatenate(keptV) if keptV else np.zeros((0, d))
     return K, V
+
+
+# ---------------------------------------------------------------------------
+# Tiered placement of stable heads -- FlexiCache summary, Method: a stable
+# head keeps only its top-K pages on the GPU, the rest in host memory, and a
+# rerank brings over only the pages newly promoted into its selection;
+# unstable heads stay entirely on the GPU.  The min-max bounds of every page
+# stay on the GPU (Key observations, assumption 2), so scoring never reads
+# host memory.
+# ---------------------------------------------------------------------------
+
+def rerank_promotion(resident: Sequence[int], selection: Sequence[int]):
+    """Pages a rerank moves for one stable head: promoted = selected and not
+    resident (copied host -> GPU), demoted = resident and not selected
+    (their GPU slots are freed).  Afterwards the resident set is the
+    selection.  Returns (promoted, demoted), each ascending."""
+    res, sel = set(int(p) for p in resident), set(int(p) for p in selection)
+    return (np.array(sorted(sel - res), dtype=np.int64),
+            np.array(sorted(res - sel), dtype=np.int64))
+
+
+def decode_head_rerank(q_steps: np.ndarray, K: np.ndarray, V: np.ndarray, stable: bool,
+                       Ktop: int, P: int, scale: float, period: int = 16):
+    """One KV head decoded over T steps of a fixed cache with the rerank
+    schedule (no tokens appended): on a rerank step it re-selects its top-K
+    pages from the pages' bounds, otherwise it keeps the previous selection;
+    every step attends its selection.  Where the pages live (GPU or host)
+    does not change the result.  Returns (outputs [T][Gq][d], selections)."""
+    kmin, kmax = page_minmax(np.asarray(K, dtype=np.float64), P)
+    sel, outs, sels = None, [], []
+    for t in range(q_steps.shape[0]):
+        if rerank_due(t, stable, period):
+            sel = topk_pages(page_scores(q_steps[t], kmin, kmax), Ktop)
+        outs.append(decode_head(q_steps[t], K, V, sel, P, scale))
+        sels.append(np.array(sel, dtype=np.int64))
+    return np.stack(outs), sels

@@ -502,3 +502,35 @@ def test_prefill_one_chunk_full_budget_and_brute_force():
         best = max(itertools.combinations(range(12), k),
                    key=lambda c: (sum(s[list(c)]), [-t for t in c]))
         assert O.top_tokens(s, k).tolist() == list(best)
+
+
+# ------------------------------------------------ tiered placement ---------
+
+def test_rerank_promotion_sets():
+    """After a rerank the resident set is the selection: promoted and the
+    kept pages make up the selection, demoted and kept the old residents."""
+    rng = np.random.default_rng(4)
+    for _ in range(200):
+        npg = int(rng.integers(1, 60))
+        old = rng.choice(npg, size=int(rng.integers(0, npg + 1)), replace=False)
+        new = rng.choice(npg, size=int(rng.integers(0, npg + 1)), replace=False)
+        pro, dem = O.rerank_promotion(old, new)
+        kept = set(old.tolist()) & set(new.tolist())
+        assert set(pro.tolist()) | kept == set(new.tolist()) and not set(pro.tolist()) & kept
+        assert set(dem.tolist()) | kept == set(old.tolist()) and not set(dem.tolist()) & kept
+        assert list(pro) == sorted(pro) and list(dem) == sorted(dem)
+    assert O.rerank_promotion([], [3, 1])[0].tolist() == [1, 3]          # first rerank
+    assert O.rerank_promotion([2, 5], [2, 5])[0].size == 0                 # nothing moves
+
+
+def test_decode_rerank_stable_head_keeps_pages_between_reranks():
+    """Hand-checkable: two single-token pages, K = 1.  The query points at
+    page 0 on step 0 and at page 1 on step 1; a stable head (period 2) keeps
+    page 0 on step 1, an unstable one moves; on step 2 both re-select."""
+    K = np.array([[1.0], [-1.0]]); V = np.array([[10.0], [20.0]])
+    q = np.array([[[1.0]], [[-1.0]], [[-1.0]]])
+    o_s, s_s = O.decode_head_rerank(q, K, V, True, 1, 1, 1.0, period=2)
+    o_u, s_u = O.decode_head_rerank(q, K, V, False, 1, 1, 1.0, period=2)
+    assert [s.tolist() for s in s_s] == [[0], [0], [1]]
+    assert [s.tolist() for s in s_u] == [[0], [1], [1]]
+    assert o_s[:, 0, 0].tolist() == [10.0, 10.0, 20.0] and o_u[:, 0, 0].tolist() == [10.0, 20.0, 20.0]
