@@ -12,8 +12,11 @@
  *       method (sparse decode, Quest-style min-max page bound), Method
  *       (stable and unstable heads, rerank every 16 steps for stable heads,
  *       no scoring between reranks), System engineering (per-head-layer
- *       block table with null blocks), Key observations, assumption 2
- *       (GPU-resident MinMax cache).
+ *       block table with null blocks; physical block reuse in the
+ *       rerank kernel; transfer kernel over pinned host memory), Key
+ *       observations, assumption 2 (GPU-resident MinMax cache), tiered
+ *       placement (stable heads keep their top-K pages on the GPU, the
+ *       rest in host memory; only newly promoted pages move).
  *
  * Conventions shared by every call
  *   - Return value: KVS_OK (0) or a negative KVS_E* code.  On error no kernel
@@ -31,7 +34,8 @@
  *   - Contents of device-resident integer inputs (seq_len, page_table,
  *     meta_base, sel) cannot be checked before launch.  Kernels never read
  *     outside the buffers described here: a page id outside [0, num_pages)
- *     or a negative id is treated as a null page and skipped, as is a
+ *     or a negative id is treated as a null page and skipped (only scoring
+ *     and the host tier calls tell KVS_PAGE_ON_HOST apart), as is a
  *     min-max block outside [0, num_meta); seq_len is clamped to
  *     [0, P*max_group_pages]; sel_count is clamped to [0, K].
  */
@@ -54,6 +58,11 @@ enum {
 };
 
 enum { KVS_F16 = 0, KVS_BF16 = 1 };
+
+/* Page-table entry of a logical page whose K/V lives only in the host tier
+ * (kvs_host_tier): its bounds are on the GPU, so it is scored like a
+ * resident page, but the decode skips it until kvs_promote_pages maps it. */
+#define KVS_PAGE_ON_HOST (-2)
 
 /*
  * One layer's head-ragged paged KV cache [T 3.2; F System engineering].
@@ -79,8 +88,10 @@ enum { KVS_F16 = 0, KVS_BF16 = 1 };
  *   meta_base   device, [b][Hkv] int32: first minmax block of each head; the
  *               head's run holds ceil(n/P) blocks.
  *   page_table  device, [b][G][max_group_pages] int32 physical page ids;
- *               -1 marks a null entry [F System engineering].  Logical page
- *               p of head h covers its tokens [p*P, (p+1)*P).
+ *               -1 marks a null entry [F System engineering],
+ *               KVS_PAGE_ON_HOST a page held in the host tier.  Logical
+ *               page p of head h covers its tokens [p*P, (p+1)*P).  Written
+ *               only by kvs_promote_pages (tiered heads' entries).
  *   seq_len     device, [b][Hkv] int32: n, the tokens head h of request r
  *               holds (ceil(B*N) retained under Budget Reservation [T 3.1],
  *               plus the tokens appended since), 1 <= n <= P*max_group_pages.
@@ -123,7 +134,8 @@ int kvs_build_minmax(const kvs_paged_kv* cache, void* stream);
  *                     sum_c max(q[r][g][c]*kmin[c], q[r][g][c]*kmax[c])
  * (no 1/sqrt(d) scale), fp32 products of the fp16/bf16 inputs (exact) summed
  * in a fixed order.  Pages p >= ceil(n/P), pages with a null table entry and
- * pages whose block is outside [0, num_meta) get -inf.
+ * pages whose block is outside [0, num_meta) get -inf; a KVS_PAGE_ON_HOST
+ * page is scored from its bounds like a resident one.
  *   q       device, [b][Hq][d] dtype; query head g belongs to KV head g/Gq.
  *   scores  device, [b][Hkv][max_group_pages] fp32, fully written.
  * Supported sizes: b*Hkv <= 16383 and b*Hkv*max_group_pages < 2^31
@@ -219,6 +231,76 @@ int kvs_prefill_chunk(const kvs_paged_kv* cache, const void* k_chunk, const void
 /* Bytes of workspace kvs_prefill_chunk needs (per head: its length before
  * the chunk, its quota and the kept positions).  0 on bad arguments. */
 size_t kvs_prefill_workspace_bytes(int32_t b, int32_t Hkv, int32_t C);
+
+/*
+ * Host tier of a cache whose stable heads keep only their selected pages on
+ * the GPU [F tiered placement].  Needs Hp == 1, so that every head has a
+ * page table of its own.  A tiered head (host_base[r][h] >= 0) has every
+ * logical page p < ceil(n/P) in host memory at host page host_base[r][h] + p
+ * and owns `slots` GPU pages; its table entry for p is the physical id of
+ * the slot holding p when p is resident and KVS_PAGE_ON_HOST otherwise.
+ * Heads with host_base < 0 are not tiered and keep all pages on the GPU.
+ *   host_kv         pinned host memory allocated by hipHostMalloc (torch's
+ *                   pin_memory allocator is one), [num_host_pages][2][P][d]
+ *                   dtype: the same K-then-V tile as a GPU page.  Kernels
+ *                   read and write it directly over the host link; the
+ *                   call checks that the pointer is pinned host memory
+ *                   mapped for the device and fails with KVS_EINVAL if not.
+ *                   It cannot check the size: the caller guarantees
+ *                   num_host_pages pages.
+ *   host_base       device, [b][Hkv] int64.
+ *   slot_page       device, [b][Hkv][slots] int32: the logical page held by
+ *                   each GPU slot of the head, -1 when free.  Written only by
+ *                   kvs_promote_pages.
+ *   slot_phys       device, [b][Hkv][slots] int32: the physical page of each
+ *                   slot (ids outside [0, num_pages) mark unusable slots).
+ *   slots           GPU pages per tiered head, 1 <= slots <= 1024.
+ *   num_host_pages  pages in host_kv, 1 <= num_host_pages < 2^31.
+ */
+typedef struct kvs_host_tier {
+  void* host_kv;
+  const int64_t* host_base;
+  int32_t* slot_page;
+  const int32_t* slot_phys;
+  int32_t slots;
+  int64_t num_host_pages;
+} kvs_host_tier;
+
+/*
+ * Bulk offload after prefill [F tiered placement]: for every tiered head,
+ * every page p < ceil(n/P) whose table entry is a physical page is copied
+ * from the GPU to host page host_base[r][h] + p.  Reads only host_kv,
+ * host_base and num_host_pages of the tier; the table is not changed (the
+ * caller remaps the head once the copy has completed on `stream`).  Host
+ * pages outside [0, num_host_pages) are skipped.  Needs b*Hkv <= 65535.
+ */
+int kvs_offload_pages(const kvs_paged_kv* cache, const kvs_host_tier* tier, void* stream);
+
+/*
+ * Promotion after a rerank [F tiered placement; physical block reuse in the
+ * rerank kernel; transfer kernel over pinned host memory].  For every tiered
+ * head h with heads[h] != 0 (heads: host array [Hkv], NULL = every head)
+ * and the selection sel[r][h][0 .. sel_count) of kvs_topk_pages:
+ *   - a slot whose page is not selected is freed; that page's entry becomes
+ *     KVS_PAGE_ON_HOST (p < ceil(n/P)) or -1 (beyond);
+ *   - a selected page p < ceil(n/P) whose entry is KVS_PAGE_ON_HOST is
+ *     promoted: copied from host page host_base[r][h] + p into a free slot
+ *     (free slots in slot order, promoted pages in ascending page order),
+ *     whose physical id becomes the entry; pages already resident stay
+ *     where they are, so only the set difference crosses the host link.
+ * Afterwards every selected page of the head is resident and no other page
+ * is, provided slots >= K.  Heads not tiered or not in `heads` are left as
+ * they are.
+ *   sel, sel_count  device, as written by kvs_topk_pages with this K.
+ *   K               1 <= K <= slots.
+ *   moved           device, [b][Hkv] int32 or NULL: pages copied per head
+ *                   (0 for heads left as they are).
+ * Needs max_group_pages <= 8192 and b*Hkv <= 2^31 - 1.  Calls overlapping
+ * on one cache race; the decode after it must be ordered after it.
+ */
+int kvs_promote_pages(const kvs_paged_kv* cache, const kvs_host_tier* tier, const int32_t* sel,
+                      const int32_t* sel_count, int32_t K, const uint8_t* heads, int32_t* moved,
+                      void* stream);
 
 /*
  * Ahead-of-time workload split map [T 3.3], host only.

@@ -237,6 +237,82 @@ extern "C" int kvs_append_kv(const kvs_paged_kv* cache, const void* k_new, const
 }
 
 namespace {
+// Validates the host tier of a cache: first the descriptor's fields, then
+// (the one HIP call, made after every other check of the entry point) that
+// host_kv is pinned host memory mapped for the current device, whose device
+// address goes to the kernels.
+int check_tier_fields(const kvs_host_tier* p, const CacheView& c, const char* fn) {
+  if (!p) return set_error(KVS_EINVAL, "%s: tier descriptor is NULL", fn);
+  if (!p->host_kv || !p->host_base || !p->slot_page || !p->slot_phys)
+    return set_error(KVS_EINVAL, "%s: null pointer in tier descriptor", fn);
+  if (c.Hp != 1) return set_error(KVS_EUNSUPPORTED, "%s: a host tier needs Hp == 1", fn);
+  if (p->slots < 1 || p->slots > kMaxSlots)
+    return set_error(KVS_EINVAL, "%s: slots=%d not in [1, %d]", fn, p->slots, kMaxSlots);
+  if (p->num_host_pages < 1 || p->num_host_pages > 0x7fffffff)
+    return set_error(KVS_EINVAL, "%s: num_host_pages not in [1, 2^31)", fn);
+  if (!aligned16(p->host_kv)) return set_error(KVS_EINVAL, "%s: host_kv must be 16-byte aligned", fn);
+  return KVS_OK;
+}
+
+int map_tier(const kvs_host_tier* p, const char* fn, HostTierView* t) {
+  hipPointerAttribute_t a;
+  const hipError_t e = hipPointerGetAttributes(&a, p->host_kv);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();   // leave no error behind for the caller's next call
+    return set_error(KVS_EINVAL, "%s: host_kv is not memory known to HIP (%s)", fn,
+                     hipGetErrorString(e));
+  }
+  if (a.type != hipMemoryTypeHost || !a.devicePointer)
+    return set_error(KVS_EINVAL, "%s: host_kv is not pinned host memory mapped for the device",
+                     fn);
+  t->host_kv = a.devicePointer;
+  t->host_base = p->host_base;
+  t->slot_page = p->slot_page;
+  t->slot_phys = p->slot_phys;
+  t->slots = p->slots;
+  t->num_host_pages = p->num_host_pages;
+  return KVS_OK;
+}
+}  // namespace
+
+extern "C" int kvs_offload_pages(const kvs_paged_kv* cache, const kvs_host_tier* tier,
+                                 void* stream) {
+  clear_error();
+  static const char* fn = "kvs_offload_pages";
+  CacheView c;
+  if (int rc = check_cache(cache, false, fn, &c)) return rc;
+  if ((int64_t)c.b * c.Hkv > 65535) return set_error(KVS_EUNSUPPORTED, "%s: b*Hkv > 65535", fn);
+  if (int rc = check_tier_fields(tier, c, fn)) return rc;
+  HostTierView t;
+  if (int rc = map_tier(tier, fn, &t)) return rc;
+  if (hipError_t e = launch_offload(c, t, (hipStream_t)stream)) return hip_error(e, fn);
+  return KVS_OK;
+}
+
+extern "C" int kvs_promote_pages(const kvs_paged_kv* cache, const kvs_host_tier* tier,
+                                 const int32_t* sel, const int32_t* sel_count, int32_t K,
+                                 const uint8_t* heads, int32_t* moved, void* stream) {
+  clear_error();
+  static const char* fn = "kvs_promote_pages";
+  CacheView c;
+  if (int rc = check_cache(cache, false, fn, &c)) return rc;
+  if (!sel || !sel_count) return set_error(KVS_EINVAL, "%s: null sel or sel_count", fn);
+  if (c.maxpg > kMaxTierPages)
+    return set_error(KVS_EUNSUPPORTED, "%s: max_group_pages=%d > %d", fn, c.maxpg, kMaxTierPages);
+  if ((int64_t)c.b * c.Hkv > 0x7fffffff) return set_error(KVS_EINVAL, "%s: b*Hkv too large", fn);
+  if (int rc = check_tier_fields(tier, c, fn)) return rc;
+  if (K < 1 || K > tier->slots)
+    return set_error(KVS_EINVAL, "%s: K=%d not in [1, slots=%d]", fn, K, tier->slots);
+  HeadMask m = every_head();
+  if (heads && head_subset(heads, c.Hkv, &m, fn)) return KVS_EINVAL;
+  HostTierView t;
+  if (int rc = map_tier(tier, fn, &t)) return rc;
+  if (hipError_t e = launch_promote(c, t, sel, sel_count, K, m, moved, (hipStream_t)stream))
+    return hip_error(e, fn);
+  return KVS_OK;
+}
+
+namespace {
 // Checks S_row and fills the split prefix sums; returns Smax via *smax.
 int check_splits(const int32_t* S_row, int G, int b, DecodeArgs* a, int* smax, const char* fn) {
   if (!S_row) return set_error(KVS_EINVAL, "%s: S_row is NULL", fn);

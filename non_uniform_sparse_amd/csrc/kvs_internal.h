@@ -17,7 +17,9 @@ constexpr int kMaxTopkPages = 8192;
 constexpr int kMaxK = 1024;
 constexpr int kMaxSplitsPerRequest = 65536;
 constexpr int kMaxScoreHeads = 16383;
-constexpr int kMaxChunk = 8192;          // prefill chunk length (16-bit kept positions)   // b * Hkv: page-count prefix held in 64 KB of LDS
+constexpr int kMaxChunk = 8192;          // prefill chunk length (16-bit kept positions)
+constexpr int kMaxSlots = 1024;          // GPU pages per tiered head
+constexpr int kMaxTierPages = 8192;      // max_group_pages of a tiered cache (LDS bitmap)
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Records a message for kvs_last_error() and returns `code`.
@@ -43,6 +45,17 @@ struct HeadMask {
   __host__ __device__ bool has(int h) const {
     return all != 0u || (h >= 0 && h < kMaxHkv && ((w[h >> 5] >> (h & 31)) & 1u));
   }
+};
+
+// A validated kvs_host_tier; host_kv is the device address of the pinned
+// host pages.
+struct HostTierView {
+  void* host_kv;
+  const int64_t* host_base;
+  int32_t* slot_page;
+  const int32_t* slot_phys;
+  int slots;
+  int64_t num_host_pages;
 };
 
 struct DecodeArgs {
@@ -74,6 +87,10 @@ hipError_t launch_prefill(const CacheView& c, const void* k_chunk, const void* v
                           const float* scores, const int32_t* quota, int C, void* ws,
                           hipStream_t s);
 size_t prefill_workspace_bytes(int b, int Hkv, int C);
+hipError_t launch_offload(const CacheView& c, const HostTierView& t, hipStream_t s);
+hipError_t launch_promote(const CacheView& c, const HostTierView& t, const int32_t* sel,
+                          const int32_t* sel_count, int K, const HeadMask& heads, int32_t* moved,
+                          hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s);
 // Resident decode workgroups per compute unit for a kernel variant.

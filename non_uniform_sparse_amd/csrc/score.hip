@@ -126,7 +126,8 @@ __global__ __launch_bounds__(kThreads) void score_kernel(CacheView c, const uint
         }
         const int p = p0 + rd * RP + u * PPW + pp;
         const int64_t m = mb + p;
-        const bool ok = head_ok && pt[u] >= 0 && pt[u] < c.num_pages && m >= 0 && m <= last;
+        const bool present = (pt[u] >= 0 && pt[u] < c.num_pages) || pt[u] == KVS_PAGE_ON_HOST;
+        const bool ok = head_ok && present && m >= 0 && m <= last;
         if (ql == 0 && p < p1) out[p] = ok ? best : -__builtin_inff();
       }
     };

@@ -21,11 +21,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvs.so")
 
 KVS_OK, KVS_EINVAL, KVS_EUNSUPPORTED, KVS_EHIP, KVS_ENOSPC = 0, -1, -2, -3, -4
 KVS_F16, KVS_BF16 = 0, 1
+KVS_PAGE_ON_HOST = -2
 
 # Every symbol include/kvs.h declares.
 EXPORTS = (
     "kvs_build_minmax", "kvs_score_pages", "kvs_score_pages_heads", "kvs_topk_pages",
     "kvs_topk_pages_heads", "kvs_append_kv", "kvs_prefill_chunk", "kvs_prefill_workspace_bytes",
+    "kvs_offload_pages", "kvs_promote_pages",
     "kvs_plan_split",
     "kvs_decode_attn",
     "kvs_decode_workspace_bytes", "kvs_decode_concurrency", "kvs_cluster_heads",
@@ -51,6 +53,17 @@ class PagedKV(ctypes.Structure):
         ("Hp", ctypes.c_int32), ("d", ctypes.c_int32), ("P", ctypes.c_int32),
         ("max_group_pages", ctypes.c_int32), ("num_pages", ctypes.c_int32),
         ("num_meta", ctypes.c_int32), ("dtype", ctypes.c_int32),
+    ]
+
+
+class HostTier(ctypes.Structure):
+    _fields_ = [
+        ("host_kv", ctypes.c_void_p),
+        ("host_base", ctypes.c_void_p),
+        ("slot_page", ctypes.c_void_p),
+        ("slot_phys", ctypes.c_void_p),
+        ("slots", ctypes.c_int32),
+        ("num_host_pages", ctypes.c_int64),
     ]
 
 
@@ -85,6 +98,9 @@ def lib() -> ctypes.CDLL:
         L.kvs_prefill_chunk.argtypes = [pkv, vp, vp, vp, vp, i32, vp, ctypes.c_size_t, vp]
         L.kvs_prefill_workspace_bytes.argtypes = [i32, i32, i32]
         L.kvs_prefill_workspace_bytes.restype = ctypes.c_size_t
+        ptier = ctypes.POINTER(HostTier)
+        L.kvs_offload_pages.argtypes = [pkv, ptier, vp]
+        L.kvs_promote_pages.argtypes = [pkv, ptier, vp, vp, i32, vp, vp, vp]
         L.kvs_plan_split.argtypes = [vp, vp, i32, i32, i32, f64, i32, vp]
         L.kvs_decode_attn.argtypes = [pkv, vp, vp, vp, i32, vp, f32, vp, ctypes.c_size_t, vp, vp]
         L.kvs_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, vp, i32]
@@ -225,6 +241,54 @@ def kvs_append_kv(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor, stream
     _need(k_new, "k_new", (s.b, s.Hkv, s.d), cache.kv.dtype, dev)
     _need(v_new, "v_new", (s.b, s.Hkv, s.d), cache.kv.dtype, dev)
     _check(lib().kvs_append_kv(ctypes.byref(s), _ptr(k_new), _ptr(v_new), _stream(stream)))
+
+
+@dataclass
+class Tier:
+    """Host tier of one layer's cache (the fields of kvs_host_tier)."""
+    host_kv: torch.Tensor       # pinned host [num_host_pages][2][P][d]
+    host_base: torch.Tensor     # int64 [b][Hkv], -1: head not tiered
+    slot_page: torch.Tensor     # int32 [b][Hkv][slots], -1 free
+    slot_phys: torch.Tensor     # int32 [b][Hkv][slots]
+
+    def struct(self, cache: Cache) -> HostTier:
+        b, Hkv = cache.seq_len.shape
+        dev = cache.kv.device
+        _, _, two, P, d = cache.kv.shape
+        if not self.host_kv.is_pinned():
+            raise ValueError("host_kv must be pinned host memory")
+        _need(self.host_kv, "host_kv", (self.host_kv.shape[0], 2, P, d), cache.kv.dtype,
+              torch.device("cpu"))
+        slots = self.slot_page.shape[2]
+        _need(self.host_base, "host_base", (b, Hkv), torch.int64, dev)
+        _need(self.slot_page, "slot_page", (b, Hkv, slots), torch.int32, dev)
+        _need(self.slot_phys, "slot_phys", (b, Hkv, slots), torch.int32, dev)
+        return HostTier(self.host_kv.data_ptr(), self.host_base.data_ptr(),
+                        self.slot_page.data_ptr(), self.slot_phys.data_ptr(), slots,
+                        self.host_kv.shape[0])
+
+
+def kvs_offload_pages(cache: Cache, tier: Tier, stream=None) -> None:
+    """Copy every resident page of the tiered heads to its host page."""
+    s, t = cache.struct(), tier.struct(cache)
+    _check(lib().kvs_offload_pages(ctypes.byref(s), ctypes.byref(t), _stream(stream)))
+
+
+def kvs_promote_pages(cache: Cache, tier: Tier, sel: torch.Tensor, sel_count: torch.Tensor,
+                      K: int, heads=None, moved: Optional[torch.Tensor] = None,
+                      stream=None) -> None:
+    """Make the selection of the tiered heads (heads=None: every head)
+    resident, moving only the newly selected pages from the host tier."""
+    s, t = cache.struct(), tier.struct(cache)
+    dev = cache.kv.device
+    _need(sel, "sel", (s.b, s.Hkv, K), torch.int32, dev)
+    _need(sel_count, "sel_count", (s.b, s.Hkv), torch.int32, dev)
+    if moved is not None:
+        _need(moved, "moved", (s.b, s.Hkv), torch.int32, dev)
+    h = None if heads is None else _heads(heads, s.Hkv)
+    _check(lib().kvs_promote_pages(ctypes.byref(s), ctypes.byref(t), _ptr(sel), _ptr(sel_count),
+                                   K, None if h is None else h.ctypes.data, _ptr(moved),
+                                   _stream(stream)))
 
 
 def kvs_prefill_workspace_bytes(b: int, Hkv: int, C: int) -> int:

@@ -236,3 +236,34 @@ def test_rerank_schedule_matches_oracle():
         for t in range(40):
             want = [O.rerank_due(t, bool(s), period) for s in stable]
             assert heads_due(t, stable, period).tolist() == want
+
+
+# ------------------------------------------------------------ host tier --
+
+def test_tier_validation_before_any_hip_call():
+    """Every descriptor check of the host-tier calls comes before the pinned
+    pointer query (the only HIP call ahead of the launch)."""
+    L = _lib()
+    s = _FakeCache(Hp=1).s
+    tier = lambda **k: kvs.HostTier(**{**dict(host_kv=0x900000, host_base=0x10000,
+                                              slot_page=0x20000, slot_phys=0x30000, slots=64,
+                                              num_host_pages=100), **k})
+    prom = lambda s_, t, K=64: L.kvs_promote_pages(ctypes.byref(s_), ctypes.byref(t), 0x40000,
+                                                   0x50000, K, None, None, None)
+    assert prom(_FakeCache(Hp=4).s, tier()) == kvs.KVS_EUNSUPPORTED        # needs one head per table
+    assert prom(s, tier(slots=0)) == kvs.KVS_EINVAL
+    assert prom(s, tier(slots=2000)) == kvs.KVS_EINVAL
+    assert prom(s, tier(num_host_pages=0)) == kvs.KVS_EINVAL
+    assert prom(s, tier(host_kv=0x900008)) == kvs.KVS_EINVAL              # misaligned
+    assert prom(s, tier(slot_phys=0)) == kvs.KVS_EINVAL
+    assert prom(s, tier(), K=65) == kvs.KVS_EINVAL                         # K > slots
+    assert prom(s, tier(), K=0) == kvs.KVS_EINVAL
+    assert prom(_FakeCache(Hp=1, max_group_pages=9000).s, tier()) == kvs.KVS_EUNSUPPORTED
+    assert L.kvs_promote_pages(ctypes.byref(s), None, 0x40000, 0x50000, 64, None, None,
+                               None) == kvs.KVS_EINVAL
+    assert L.kvs_promote_pages(ctypes.byref(s), ctypes.byref(tier()), None, 0x50000, 64, None,
+                               None, None) == kvs.KVS_EINVAL
+    assert L.kvs_offload_pages(ctypes.byref(_FakeCache(Hp=2).s), ctypes.byref(tier()),
+                               None) == kvs.KVS_EUNSUPPORTED
+    assert L.kvs_offload_pages(ctypes.byref(s), None, None) == kvs.KVS_EINVAL
+    assert "tier" in kvs.last_error()
