@@ -232,6 +232,122 @@ def prefill_report(configs, chunk: int = 2048) -> dict:
     return out
 
 
+def tier_report(name: str = "flexicache_topk", period: int = 16, windows: int = 3,
+                unstable_frac: float = 0.25) -> dict:
+    """Tiered placement of stable heads (FlexiCache summary, tiered
+    placement), one page table per head.  Times, with events behind a short
+    GPU spin: the bulk offload of the stable heads' pages after prefill
+    (GPU -> pinned host), the promotion after each rerank (host -> GPU, only
+    newly selected pages), and whole rerank windows of ``period`` steps on
+    the tiered and on the fully resident cache.  The host-link figures are
+    set against a plain pinned-to-device copy of 256 MiB measured here."""
+    from non_uniform_sparse_amd.tiered import TieredLoop
+    from non_uniform_sparse_amd.kvs import Tier
+    stream = torch.cuda.current_stream()
+    rate = sleep_rate(stream)
+
+    def timed(fn, spin_ms=0.3):
+        torch.cuda._sleep(int(rate * spin_ms))
+        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b_.record()
+        b_.synchronize()
+        return a.elapsed_time(b_)
+
+    # plain copies over the host link, both directions
+    n = 256 << 20
+    h = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+    h.fill_(1)
+    dbuf = torch.empty(n, dtype=torch.uint8, device="cuda")
+    h2d = min(timed(lambda: dbuf.copy_(h, non_blocking=True)) for _ in range(5))
+    d2h = min(timed(lambda: h.copy_(dbuf, non_blocking=True)) for _ in range(5))
+    del h, dbuf
+    copy_h2d, copy_d2h = n / (h2d * 1e-3) / 1e9, n / (d2h * 1e-3) / 1e9
+
+    wl = make_workload(name, Hp=1)
+    c = wl.cfg
+    steps = period * windows + 1
+    page_bytes = 2 * c.P * c.d * 2
+    # bulk offload, timed on a fully resident cache of its own
+    full = DecodeStep(wl, device="cuda", poison=False)
+    stable = wl.stable_heads(unstable_frac)
+    npg = -(-wl.n // c.P)                                         # [b][L][Hkv]
+    off_ms, off_pages = 0.0, 0
+    for l in range(c.L):
+        hb = np.full((c.b, c.Hkv), -1, dtype=np.int64)
+        run = 0
+        for r in range(c.b):
+            for hh in range(c.Hkv):
+                if stable[l, hh]:
+                    hb[r, hh] = run
+                    run += int(npg[r, l, hh])
+        host = torch.empty((max(1, run), 2, c.P, c.d), dtype=full.caches[l].kv.dtype,
+                           pin_memory=True)
+        dummy = torch.full((c.b, c.Hkv, 1), -1, dtype=torch.int32, device="cuda")
+        tier = Tier(host, torch.from_numpy(hb).to("cuda"), dummy, dummy)
+        off_ms += timed(lambda: kvs.kvs_offload_pages(full.caches[l], tier))
+        off_pages += run
+        del host
+    del full
+    torch.cuda.empty_cache()
+
+    res = {}
+    for mode in ("tiered", "resident"):
+        loop = TieredLoop(wl, steps, period=period, tiered=mode == "tiered", stable=stable)
+        if mode == "tiered":
+            gpu_b, full_b = loop.gpu_bytes, loop.full_bytes
+        prom = []
+        for t in range(steps):
+            if mode == "tiered" and t % period == 0:
+                due = [loop.select(t, l) for l in range(c.L)]
+                torch.cuda.synchronize()
+                ms = timed(lambda: [loop.promote(l, due[l]) for l in range(c.L)])
+                moved = sum(int(m.sum().item()) for m in loop.moved)
+                prom.append((t, ms, moved))
+                for l in range(c.L):
+                    loop.ds.attend(l, loop.q[t][l])
+            else:
+                loop.run_step(t)
+        torch.cuda.synchronize()
+        # whole windows from the start, replayed as one graph
+        g = loop.capture(steps - 1)
+        wms = []
+        for _ in range(4):
+            loop.rewind()
+            torch.cuda.synchronize()
+            wms.append(timed(g.replay, spin_ms=1.0))
+        res[mode] = {"us_per_step": statistics.median(wms[1:]) / (steps - 1) * 1e3, "prom": prom}
+        del g, loop
+        torch.cuda.empty_cache()
+    stable_heads = c.b * int(stable.sum())
+    reranks = [{"step": t, "pages_moved": m,
+                "frac_of_topk": round(m / (stable_heads * c.topk), 3),
+                "us": round(ms * 1e3, 1),
+                "GBps": round(m * page_bytes / (ms * 1e-3) / 1e9, 2)}
+               for t, ms, m in res["tiered"]["prom"]]
+    later = [r for r in reranks if r["step"] > 0]
+    return {
+        "config": {"workload": name, "requests": c.b, "layers": c.L, "kv_heads": c.Hkv,
+                   "tokens": c.N, "topk_pages": c.topk, "page_bytes": page_bytes,
+                   "heads_per_page_table": 1, "period": period,
+                   "stable_heads": f"{int(stable.sum())} of {c.L * c.Hkv} per request"},
+        "gpu_kv_bytes": {"tiered": gpu_b, "resident": full_b,
+                         "saved": round(1 - gpu_b / full_b, 3)},
+        "host_link": {"copy_h2d_GBps": round(copy_h2d, 1), "copy_d2h_GBps": round(copy_d2h, 1),
+                      "nominal_GBps": 64.0, "note": "PCIe 5.0 x16, one direction"},
+        "offload": {"pages": off_pages, "us": round(off_ms * 1e3, 1),
+                    "GBps": round(off_pages * page_bytes / (off_ms * 1e-3) / 1e9, 2)},
+        "promotion": reranks,
+        "promotion_later_reranks_GBps": round(statistics.mean([r["GBps"] for r in later]), 2)
+        if later else None,
+        "us_per_step": {"tiered": round(res["tiered"]["us_per_step"], 1),
+                        "resident": round(res["resident"]["us_per_step"], 1)},
+        "window": f"steps 0..{steps - 2} as one graph: {windows} reranks with promotion, the "
+                  "other steps scoring only unstable heads",
+    }
+
+
 def skew_report(configs, launches: int = 20) -> dict:
     """Per-workgroup duration skew of the split-K decode kernel, max / mean
     over the workgroups of one launch, median over launches, per layer; with
@@ -308,6 +424,9 @@ def main() -> int:
                     help="time decoding over steps with stability-aware reranking against "
                          "reranking every step (default configs: flexicache_topk, gemma3_mixed "
                          "at 8 layers) and print that record instead of the step line")
+    ap.add_argument("--tier", nargs="?", const="flexicache_topk", default=None, metavar="CONFIG",
+                    help="time tiered placement of stable heads (offload, promotion over the "
+                         "host link, rerank windows tiered vs resident), print it and exit")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--skew", nargs="*", default=None, metavar="CONFIG",
                     help="measure per-workgroup duration skew (planned vs uniform split "
@@ -317,8 +436,8 @@ def main() -> int:
                          "hardware byte counters, then exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the decode path here runs on a single MI355X "
-              "(see DESIGN.md for how it would shard); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the decode path here runs on a single MI355X; "
+              "run with --gpus 1", file=sys.stderr)
         return 2
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda:0"
@@ -330,6 +449,9 @@ def main() -> int:
     if args.rerank_reuse is not None:
         print(json.dumps({"rerank_reuse": rerank_reuse_report(
             args.rerank_reuse or ["flexicache_topk", "gemma3_mixed"])}))
+        return 0
+    if args.tier is not None:
+        print(json.dumps({"tier": tier_report(args.tier)}))
         return 0
     if args.skew is not None:
         print(json.dumps({"skew": skew_report(args.skew or ["llama8b_ragged", "longctx_skew"])}))
