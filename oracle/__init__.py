@@ -14,7 +14,10 @@ Sources (the pages, cited by title and section):
     Efficient KV Cache Management (MLSys 2026)" (paper summary) -- Core method
     (sparse decode, Quest-style min-max page bound), System engineering
     (per-head block table with null entries), Key observations (assumption 2,
-    GPU-resident MinMax cache).
+    GPU-resident MinMax cache), tiered placement.
+  * "CacheGen -- KV Cache Compression and Streaming" (paper notes) --
+    sections 3 and 7: change-based encoding over token groups, layer-wise
+    quantization, arithmetic coding per (channel, layer) (codec_oracle.py).
 
 Every function is pinned by ``tests/test_oracle_pins.py`` against closed
 forms, brute force or invariants; none is "parity unpinned" except the
@@ -23,3 +26,4 @@ stated goal is pinned).
 """
 
 from .kvs_oracle import *  # noqa: F401,F403
+from .codec_oracle import *  # noqa: F401,F403
