@@ -7,6 +7,10 @@
  *   [T] "Tangram: Unlocking Non-Uniform KV Cache Compression for Efficient
  *       Multi-turn LLM Serving" (paper review): 3.1 Budget Reservation,
  *       3.2 Ragged Paging, 3.3 AOT Load Balancing.
+ *   [C] "CacheGen -- KV Cache Compression and Streaming" (paper notes):
+ *       3 (change-based encoding over groups of tokens), 7 (implementation:
+ *       8-bit anchors, a delta bin per third of the layers, arithmetic
+ *       coding with statistics per channel and layer, GPU decoding).
  *   [F] "FlexiCache: Leveraging Temporal Stability of Attention Heads for
  *       Efficient KV Cache Management (MLSys 2026)" (paper summary): Core
  *       method (sparse decode, Quest-style min-max page bound), Method
@@ -354,6 +358,100 @@ size_t kvs_decode_workspace_bytes(int32_t b, int32_t Hq, int32_t Hkv, int32_t d,
  * the split map is sized to what the chip runs at once]:
  * *W = compute units x max resident workgroups per compute unit. */
 int kvs_decode_concurrency(int32_t device, int32_t d, int32_t gqa, int32_t dtype, int32_t* W);
+
+/*
+ * KV-cache codec [C 3, 7]: one chunk of T tokens of every layer,
+ *     x[L][2][T][C] fp16 (index 1: 0 = K, 1 = V; C = all KV heads' channels
+ *     of a token side by side),
+ * coded as follows.
+ *   - Token t is the anchor of its group iff t % group == 0.  An anchor is
+ *     kept at 8 bits: code = round((x - lo) / scale) in [0, 255], with lo and
+ *     hi the min and max of the chunk's anchors of that (layer, K/V,
+ *     channel) and scale = (hi - lo) / 255 (0 for a constant channel: code
+ *     0).  Any other token stores q = round((x - x_anchor) / bin) clamped to
+ *     [-127, 127] against its group's original anchor value, with
+ *     bin = bins[floor(3 l / L)] for layer l.  Rounding is half to even,
+ *     all in IEEE float32.
+ *   - Decoded values: an anchor is lo + code*scale; another token is its
+ *     anchor's decoded value + q*bin; float32, product then sum, rounded once
+ *     to fp16.
+ *   - Every (layer, K/V, channel) has two frequency tables, kind 0 for
+ *     anchors and 1 for deltas, built from the chunk's own symbols: over the
+ *     symbols first .. first + n - 1 (the smallest to the largest present),
+ *     floor(count * 2^16 / total), at least 1 for a present symbol, 0 for an
+ *     absent one; the rounding difference goes to the largest frequency
+ *     (ties: the lowest symbol).  A kind with no symbols has the single
+ *     symbol 0 at 2^16.
+ *   - A stream holds one token's symbols over S consecutive channels, in
+ *     channel order, range coded (32-bit, byte-wise, carry propagating:
+ *     r = floor(range / 2^16), renormalised while range < 2^24, five
+ *     flushing shifts), padded with zero bytes to a multiple of 4.  Streams
+ *     are stored in order ((l*2 + kv)*(C/S) + slice)*T + t.
+ */
+typedef struct kvs_codec_layout {
+  int32_t L, T, C;   /* layers, tokens, channels per token */
+  int32_t group;     /* tokens per group, 1 .. 320 (10 in [C 3]) */
+  int32_t S;         /* channels per stream: a multiple of 8 dividing C */
+  float bins[3];     /* delta bins of the layer thirds, > 0 ([C 7]: 0.5, 1, 1.5) */
+} kvs_codec_layout;
+
+/*
+ * An encoded chunk.  Table i = ((l*2 + kv)*C + c)*2 + kind.
+ *   lo, scale      [L][2][C] float32: the anchors' code range.
+ *   tab_first      [L][2][C][2] int32: first symbol of table i.
+ *   tab_n          [L][2][C][2] int32: symbols in table i (1 .. 256).
+ *   tab_off        [L][2][C][2] uint32: table i's cumulative frequencies
+ *                  start at cdf[tab_off[i]]; tables are stored in index
+ *                  order, back to back.
+ *   cdf            uint16: entry j of table i is the sum of the frequencies
+ *                  of its symbols before j (entry 0 is 0; the total 2^16
+ *                  after the last entry is implied).
+ *   cdf_len        entries of cdf (capacity on input to kvs_codec_encode,
+ *                  entries written on return).
+ *   streams        the streams' bytes; stream k is streams[stream_off[k] ..
+ *                  stream_off[k+1]).
+ *   stream_off     [L*2*(C/S)*T + 1] uint64 byte offsets (multiples of 4).
+ *   streams_len    bytes of streams (capacity on input to kvs_codec_encode,
+ *                  bytes written on return).
+ */
+typedef struct kvs_codec_chunk {
+  float* lo;
+  float* scale;
+  int32_t* tab_first;
+  int32_t* tab_n;
+  uint32_t* tab_off;
+  uint16_t* cdf;
+  uint64_t cdf_len;
+  uint8_t* streams;
+  uint64_t* stream_off;
+  uint64_t streams_len;
+} kvs_codec_chunk;
+
+/* Upper bounds of cdf_len and streams_len for a layout (host only; 0 for an
+ * invalid layout). */
+int kvs_codec_bounds(const kvs_codec_layout* layout, uint64_t* cdf_max, uint64_t* streams_max);
+
+/*
+ * Encode one chunk on the host (offline, as in [C 3]): x is host memory,
+ * every buffer of `out` host memory sized per `layout` (lo, scale:
+ * L*2*C; tab_*: L*2*C*2; stream_off: L*2*(C/S)*T + 1).  Runs on up to
+ * `threads` host threads (0: the hardware's count).  KVS_ENOSPC when
+ * cdf_len or streams_len is too small, with the sizes needed written to
+ * them; nothing else is then guaranteed written.
+ */
+int kvs_codec_encode(const kvs_codec_layout* layout, const uint16_t* x, kvs_codec_chunk* out,
+                     int32_t threads);
+
+/*
+ * Decode one chunk on the GPU [C 7]: every buffer of `chunk` is device
+ * memory holding what kvs_codec_encode wrote; out is device
+ * [L][2][T][C] fp16, fully written.  One lane decodes one stream; the
+ * kernel never reads outside the buffers described by cdf_len and
+ * streams_len (a corrupt stream decodes to garbage, not a fault).
+ * Needs C/S*L*2 <= 65535 workgroup rows and T <= 2^31 / 2.
+ */
+int kvs_codec_decode(const kvs_codec_layout* layout, const kvs_codec_chunk* chunk, void* out,
+                     void* stream);
 
 /* Budget-aware clustering [T 3.2], host only: per layer, heads ordered by
  * budget (largest first, equal budgets by lower head index); the head at

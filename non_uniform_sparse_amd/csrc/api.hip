@@ -236,6 +236,23 @@ extern "C" int kvs_append_kv(const kvs_paged_kv* cache, const void* k_new, const
   return KVS_OK;
 }
 
+extern "C" int kvs_codec_decode(const kvs_codec_layout* layout, const kvs_codec_chunk* chunk,
+                                void* out, void* stream) {
+  clear_error();
+  static const char* fn = "kvs_codec_decode";
+  if (int rc = codec_check_layout(layout, fn)) return rc;
+  if (!chunk || !out) return set_error(KVS_EINVAL, "%s: null chunk or output", fn);
+  if (!chunk->lo || !chunk->scale || !chunk->tab_first || !chunk->tab_n || !chunk->tab_off ||
+      !chunk->cdf || !chunk->streams || !chunk->stream_off || chunk->cdf_len < 1)
+    return set_error(KVS_EINVAL, "%s: null pointer or empty table pool in chunk", fn);
+  if (!aligned16(out)) return set_error(KVS_EINVAL, "%s: out must be 16-byte aligned", fn);
+  if (reinterpret_cast<uintptr_t>(chunk->streams) & 3)
+    return set_error(KVS_EINVAL, "%s: streams must be 4-byte aligned", fn);
+  if (hipError_t e = launch_codec_decode(*layout, *chunk, out, (hipStream_t)stream))
+    return hip_error(e, fn);
+  return KVS_OK;
+}
+
 namespace {
 // Validates the host tier of a cache: first the descriptor's fields, then
 // (the one HIP call, made after every other check of the entry point) that

@@ -92,6 +92,11 @@ hipError_t launch_promote(const CacheView& c, const HostTierView& t, const int32
                           const int32_t* sel_count, int K, const HeadMask& heads, int32_t* moved,
                           hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+// KV-cache codec: layout validation (shared by the encoder and the decoder)
+// and the decode launch.
+int codec_check_layout(const kvs_codec_layout* p, const char* fn);
+hipError_t launch_codec_decode(const kvs_codec_layout& lay, const kvs_codec_chunk& ch, void* out,
+                               hipStream_t s);
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s);
 // Resident decode workgroups per compute unit for a kernel variant.
 hipError_t decode_blocks_per_cu(int d, int gqa, int dtype, int* blocks);

@@ -28,6 +28,7 @@ EXPORTS = (
     "kvs_build_minmax", "kvs_score_pages", "kvs_score_pages_heads", "kvs_topk_pages",
     "kvs_topk_pages_heads", "kvs_append_kv", "kvs_prefill_chunk", "kvs_prefill_workspace_bytes",
     "kvs_offload_pages", "kvs_promote_pages",
+    "kvs_codec_bounds", "kvs_codec_encode", "kvs_codec_decode",
     "kvs_plan_split",
     "kvs_decode_attn",
     "kvs_decode_workspace_bytes", "kvs_decode_concurrency", "kvs_cluster_heads",
@@ -67,6 +68,22 @@ class HostTier(ctypes.Structure):
     ]
 
 
+class CodecLayout(ctypes.Structure):
+    _fields_ = [
+        ("L", ctypes.c_int32), ("T", ctypes.c_int32), ("C", ctypes.c_int32),
+        ("group", ctypes.c_int32), ("S", ctypes.c_int32), ("bins", ctypes.c_float * 3),
+    ]
+
+
+class CodecChunk(ctypes.Structure):
+    _fields_ = [
+        ("lo", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("tab_first", ctypes.c_void_p),
+        ("tab_n", ctypes.c_void_p), ("tab_off", ctypes.c_void_p), ("cdf", ctypes.c_void_p),
+        ("cdf_len", ctypes.c_uint64), ("streams", ctypes.c_void_p),
+        ("stream_off", ctypes.c_void_p), ("streams_len", ctypes.c_uint64),
+    ]
+
+
 _lib = None
 
 
@@ -101,6 +118,11 @@ def lib() -> ctypes.CDLL:
         ptier = ctypes.POINTER(HostTier)
         L.kvs_offload_pages.argtypes = [pkv, ptier, vp]
         L.kvs_promote_pages.argtypes = [pkv, ptier, vp, vp, i32, vp, vp, vp]
+        play, pch = ctypes.POINTER(CodecLayout), ctypes.POINTER(CodecChunk)
+        L.kvs_codec_bounds.argtypes = [play, ctypes.POINTER(ctypes.c_uint64),
+                                       ctypes.POINTER(ctypes.c_uint64)]
+        L.kvs_codec_encode.argtypes = [play, vp, pch, i32]
+        L.kvs_codec_decode.argtypes = [play, pch, vp, vp]
         L.kvs_plan_split.argtypes = [vp, vp, i32, i32, i32, f64, i32, vp]
         L.kvs_decode_attn.argtypes = [pkv, vp, vp, vp, i32, vp, f32, vp, ctypes.c_size_t, vp, vp]
         L.kvs_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, vp, i32]
@@ -289,6 +311,85 @@ def kvs_promote_pages(cache: Cache, tier: Tier, sel: torch.Tensor, sel_count: to
     _check(lib().kvs_promote_pages(ctypes.byref(s), ctypes.byref(t), _ptr(sel), _ptr(sel_count),
                                    K, None if h is None else h.ctypes.data, _ptr(moved),
                                    _stream(stream)))
+
+
+@dataclass
+class Encoded:
+    """One encoded chunk: the fields of kvs_codec_chunk as tensors (host
+    after kvs_codec_encode; ``to`` copies them to a device)."""
+    layout: CodecLayout
+    lo: torch.Tensor           # float32 [L][2][C]
+    scale: torch.Tensor        # float32 [L][2][C]
+    tab_first: torch.Tensor    # int32 [L][2][C][2]
+    tab_n: torch.Tensor        # int32 [L][2][C][2]
+    tab_off: torch.Tensor      # int32 holding uint32 [L][2][C][2]
+    cdf: torch.Tensor          # int16 holding uint16 [entries]
+    streams: torch.Tensor      # uint8 [bytes]
+    stream_off: torch.Tensor   # int64 [streams + 1]
+
+    def to(self, device) -> "Encoded":
+        f = {k: getattr(self, k).to(device) for k in
+             ("lo", "scale", "tab_first", "tab_n", "tab_off", "cdf", "streams", "stream_off")}
+        return Encoded(self.layout, **f)
+
+    def struct(self) -> CodecChunk:
+        return CodecChunk(self.lo.data_ptr(), self.scale.data_ptr(), self.tab_first.data_ptr(),
+                          self.tab_n.data_ptr(), self.tab_off.data_ptr(), self.cdf.data_ptr(),
+                          self.cdf.numel(), self.streams.data_ptr(),
+                          self.stream_off.data_ptr(), self.streams.numel())
+
+    def nbytes(self) -> int:
+        """Bytes of the encoded chunk: streams, offsets, tables, ranges."""
+        return sum(t.numel() * t.element_size() for t in
+                   (self.lo, self.scale, self.tab_first, self.tab_n, self.tab_off, self.cdf,
+                    self.streams, self.stream_off))
+
+
+def codec_layout(L: int, T: int, C: int, group: int = 10, S: int = 512,
+                 bins=(0.5, 1.0, 1.5)) -> CodecLayout:
+    return CodecLayout(L, T, C, group, S, (ctypes.c_float * 3)(*bins))
+
+
+def kvs_codec_bounds(layout: CodecLayout):
+    a, b = ctypes.c_uint64(), ctypes.c_uint64()
+    _check(lib().kvs_codec_bounds(ctypes.byref(layout), ctypes.byref(a), ctypes.byref(b)))
+    return int(a.value), int(b.value)
+
+
+def kvs_codec_encode(layout: CodecLayout, x: torch.Tensor, threads: int = 0) -> Encoded:
+    """Encode x (host fp16 [L][2][T][C]) on the host."""
+    L, T, C, S = layout.L, layout.T, layout.C, layout.S
+    _need(x, "x", (L, 2, T, C), torch.float16, torch.device("cpu"))
+    cdf_max, _ = kvs_codec_bounds(layout)
+    nstreams = L * 2 * (C // S) * T
+    guess = x.numel() * 2 // 2 + 64 * nstreams
+    while True:
+        e = Encoded(layout,
+                    torch.empty((L, 2, C), dtype=torch.float32),
+                    torch.empty((L, 2, C), dtype=torch.float32),
+                    torch.empty((L, 2, C, 2), dtype=torch.int32),
+                    torch.empty((L, 2, C, 2), dtype=torch.int32),
+                    torch.empty((L, 2, C, 2), dtype=torch.int32),
+                    torch.empty(cdf_max, dtype=torch.int16),
+                    torch.empty(guess, dtype=torch.uint8),
+                    torch.empty(nstreams + 1, dtype=torch.int64))
+        s = e.struct()
+        rc = lib().kvs_codec_encode(ctypes.byref(layout), _ptr(x), ctypes.byref(s), threads)
+        if rc == KVS_ENOSPC and s.streams_len > guess:
+            guess = int(s.streams_len)
+            continue
+        _check(rc)
+        e.cdf = e.cdf[:s.cdf_len].clone()
+        e.streams = e.streams[:s.streams_len].clone()
+        return e
+
+
+def kvs_codec_decode(enc: Encoded, out: torch.Tensor, stream=None) -> None:
+    """Decode a device-resident chunk into out (device fp16 [L][2][T][C])."""
+    lay = enc.layout
+    _need(out, "out", (lay.L, 2, lay.T, lay.C), torch.float16, enc.streams.device)
+    s = enc.struct()
+    _check(lib().kvs_codec_decode(ctypes.byref(lay), ctypes.byref(s), _ptr(out), _stream(stream)))
 
 
 def kvs_prefill_workspace_bytes(b: int, Hkv: int, C: int) -> int:
