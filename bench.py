@@ -348,6 +348,66 @@ def tier_report(name: str = "flexicache_topk", period: int = 16, windows: int = 
     }
 
 
+def codec_report(name: str = "llama7b_chunk", reps: int = 10) -> dict:
+    """KV-cache codec after CacheGen (paper notes, sections 3 and 7): one
+    chunk encoded on the host, then decoded on the GPU.  The decode is timed
+    with events behind a short GPU spin (median of ``reps``); the encoded
+    chunk and, for comparison, the raw fp16 chunk are timed as single pinned
+    host-to-device copies -- the transfer the codec shrinks."""
+    from non_uniform_sparse_amd import codec
+    cfg = codec.CHUNKS[name]
+    x = codec.make_chunk(cfg)
+    lay = codec.layout_of(cfg)
+    t0 = time.perf_counter()
+    enc = kvs.kvs_codec_encode(lay, x)
+    enc_s = time.perf_counter() - t0
+    d = enc.to("cuda")
+    out = torch.empty((cfg.L, 2, cfg.T, cfg.C), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.current_stream()
+    rate = sleep_rate(stream)
+    kvs.kvs_codec_decode(d, out)
+    times = []
+    for _ in range(reps):
+        torch.cuda._sleep(int(rate * 0.5))
+        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        kvs.kvs_codec_decode(d, out)
+        b_.record()
+        b_.synchronize()
+        times.append(a.elapsed_time(b_))
+    ms = statistics.median(times)
+    raw = x.numel() * 2
+    coded = enc.nbytes()
+
+    def h2d_ms(nbytes):
+        h = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+        dd = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        best = float("inf")
+        for _ in range(3):
+            a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            dd.copy_(h, non_blocking=True)
+            b_.record()
+            b_.synchronize()
+            best = min(best, a.elapsed_time(b_))
+        return best
+
+    symbols = cfg.L * 2 * cfg.T * cfg.C
+    return {
+        "config": {"workload": name, "layers": cfg.L, "tokens": cfg.T, "channels": cfg.C,
+                   "group": cfg.group, "channels_per_stream": cfg.S, "rho": cfg.rho,
+                   "streams": cfg.L * 2 * (cfg.C // cfg.S) * cfg.T},
+        "raw_bytes": raw, "encoded_bytes": coded, "ratio": round(raw / coded, 3),
+        "bits_per_value": round(8 * coded / symbols, 3),
+        "encode_host_s": round(enc_s, 3),
+        "decode_us": round(ms * 1e3, 1),
+        "decode_out_GBps": round(raw / (ms * 1e-3) / 1e9, 1),
+        "decode_Gsymbols_per_s": round(symbols / (ms * 1e-3) / 1e9, 1),
+        "h2d_encoded_us": round(h2d_ms(coded) * 1e3, 1),
+        "h2d_raw_us": round(h2d_ms(raw) * 1e3, 1),
+    }
+
+
 def skew_report(configs, launches: int = 20) -> dict:
     """Per-workgroup duration skew of the split-K decode kernel, max / mean
     over the workgroups of one launch, median over launches, per layer; with
@@ -427,6 +487,9 @@ def main() -> int:
     ap.add_argument("--tier", nargs="?", const="flexicache_topk", default=None, metavar="CONFIG",
                     help="time tiered placement of stable heads (offload, promotion over the "
                          "host link, rerank windows tiered vs resident), print it and exit")
+    ap.add_argument("--codec", nargs="?", const="llama7b_chunk", default=None, metavar="CHUNK",
+                    help="encode a KV chunk on the host and time its GPU decode, print it "
+                         "and exit")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--skew", nargs="*", default=None, metavar="CONFIG",
                     help="measure per-workgroup duration skew (planned vs uniform split "
@@ -449,6 +512,9 @@ def main() -> int:
     if args.rerank_reuse is not None:
         print(json.dumps({"rerank_reuse": rerank_reuse_report(
             args.rerank_reuse or ["flexicache_topk", "gemma3_mixed"])}))
+        return 0
+    if args.codec is not None:
+        print(json.dumps({"codec": codec_report(args.codec)}))
         return 0
     if args.tier is not None:
         print(json.dumps({"tier": tier_report(args.tier)}))

@@ -445,7 +445,8 @@ int kvs_codec_encode(const kvs_codec_layout* layout, const uint16_t* x, kvs_code
 /*
  * Decode one chunk on the GPU [C 7]: every buffer of `chunk` is device
  * memory holding what kvs_codec_encode wrote; out is device
- * [L][2][T][C] fp16, fully written.  One lane decodes one stream; the
+ * [L][2][T][C] fp16, fully written (streams_len >= 8: every stream has at
+ * least 8 bytes).  One lane decodes one stream; the
  * kernel never reads outside the buffers described by cdf_len and
  * streams_len (a corrupt stream decodes to garbage, not a fault).
  * Needs C/S*L*2 <= 65535 workgroup rows and T <= 2^31 / 2.

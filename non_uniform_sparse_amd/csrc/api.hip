@@ -243,8 +243,9 @@ extern "C" int kvs_codec_decode(const kvs_codec_layout* layout, const kvs_codec_
   if (int rc = codec_check_layout(layout, fn)) return rc;
   if (!chunk || !out) return set_error(KVS_EINVAL, "%s: null chunk or output", fn);
   if (!chunk->lo || !chunk->scale || !chunk->tab_first || !chunk->tab_n || !chunk->tab_off ||
-      !chunk->cdf || !chunk->streams || !chunk->stream_off || chunk->cdf_len < 1)
-    return set_error(KVS_EINVAL, "%s: null pointer or empty table pool in chunk", fn);
+      !chunk->cdf || !chunk->streams || !chunk->stream_off || chunk->cdf_len < 1 ||
+      chunk->streams_len < 8)
+    return set_error(KVS_EINVAL, "%s: null pointer, empty table pool or streams in chunk", fn);
   if (!aligned16(out)) return set_error(KVS_EINVAL, "%s: out must be 16-byte aligned", fn);
   if (reinterpret_cast<uintptr_t>(chunk->streams) & 3)
     return set_error(KVS_EINVAL, "%s: streams must be 4-byte aligned", fn);

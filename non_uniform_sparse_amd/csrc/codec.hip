@@ -54,40 +54,52 @@ struct CodecArgs {
   float bins[3];
 };
 
-// Bytes of one stream, a dword at a time, the next dword in flight.
+// Bytes of one stream, most significant first in a 64-bit buffer: `avail`
+// bits are valid, and a dword is added whenever 32 or fewer remain (a symbol
+// takes at most 16), with the dword after it already in flight.  Loads are
+// unconditional, at an index clamped into the stream, so the compiler keeps
+// the next dword in flight instead of waiting on a select; a valid stream
+// never consumes what a clamped load returns (its decoder reads exactly the
+// bytes its encoder wrote).
 struct ByteReader {
   const uint32_t* base;
-  uint32_t ndw;   // whole dwords in the stream
-  uint32_t next;  // dword index of `nxt`
-  uint32_t cur, nxt;
-  int left;       // bytes left in cur
-  __device__ __forceinline__ uint32_t load(uint32_t i) const { return i < ndw ? base[i] : 0u; }
-  __device__ __forceinline__ void start(const uint8_t* streams, uint64_t b, uint64_t e) {
-    base = reinterpret_cast<const uint32_t*>(streams + b);
-    ndw = (uint32_t)((e - b) >> 2);
-    cur = load(0);
-    nxt = load(1);
-    next = 1;
-    left = 4;
-  }
-  __device__ __forceinline__ uint32_t byte() {
-    if (left == 0) {
-      cur = nxt;
+  uint32_t last;    // index of the stream's last dword
+  uint32_t next;    // dword index of `nxt`
+  uint32_t nxt;
+  uint64_t bits;
+  int avail;
+  __device__ __forceinline__ uint32_t load(uint32_t i) const { return base[i < last ? i : last]; }
+  __device__ __forceinline__ void refill() {
+    if (avail <= 32) {
+      bits |= (uint64_t)__builtin_bswap32(nxt) << (32 - avail);
+      avail += 32;
       nxt = load(++next);
-      left = 4;
     }
-    const uint32_t b = cur & 0xffu;
-    cur >>= 8;
-    --left;
-    return b;
+  }
+  // Starts a stream of ndw >= 1 dwords and returns the range decoder's first
+  // code (bytes 1-4; byte 0 is the encoder's initial held byte).
+  __device__ __forceinline__ uint32_t start(const uint32_t* p, uint32_t ndw) {
+    base = p;
+    last = ndw - 1;
+    bits = ((uint64_t)__builtin_bswap32(load(0)) << 32) | __builtin_bswap32(load(1));
+    nxt = load(2);
+    next = 2;
+    const uint32_t code = (uint32_t)(bits >> 24);
+    bits <<= 40;
+    avail = 24;
+    refill();
+    return code;
   }
 };
 
 __global__ __launch_bounds__(kMaxThreads) void codec_decode_kernel(CodecArgs a) {
   __shared__ uint16_t s_cdf[kTabEntries];
-  __shared__ int s_first[2 * kCB], s_n[2 * kCB], s_loff[2 * kCB];
+  // per table: LDS offset (bits 0-13), entries - 1 (14-21), first symbol + 128 (22-30)
+  __shared__ uint32_t s_meta[2 * kCB];
+  // per channel: binary-search steps of its anchor (bits 0-3) and delta (4-7) table
+  __shared__ uint32_t s_steps[kCB];
   __shared__ float s_lo[kCB], s_scale[kCB];
-  __shared__ uint32_t s_tile[64 * 16 * kRowDwords];   // NG * group <= 1024 rows
+  extern __shared__ uint32_t s_tile[];   // [NG * group rows][kRowDwords], sized at launch
   const int tid = threadIdx.x;
   const int g = a.group, NG = a.NG, TB = NG * g;
   const int lk = blockIdx.z;                  // l * 2 + kv
@@ -106,19 +118,26 @@ __global__ __launch_bounds__(kMaxThreads) void codec_decode_kernel(CodecArgs a) 
   const bool active = row < TB && t < a.T;
   const bool anchor = row % g == 0;
   const float bin = a.bins[(3 * l) / a.L];
+  // which kinds of table this wave searches: its step count per channel is
+  // the larger of those kinds' (uniform over the wave, a scalar loop)
+  const bool wave_anchor = __ballot(active && anchor) != 0;
+  const bool wave_delta = __ballot(active && !anchor) != 0;
+  const int step_shift = wave_anchor && !wave_delta ? 0 : (!wave_anchor ? 4 : 8);
 
   uint32_t code = 0, rng = 0xffffffffu;
   ByteReader rd;
+  rd.avail = 0;
   if (active) {
     const uint64_t s = ((uint64_t)lk * NS + slice) * (uint64_t)a.T + t;
     uint64_t b = a.stream_off[s] & ~(uint64_t)3, e = a.stream_off[s + 1] & ~(uint64_t)3;
     const uint64_t lim = a.streams_len & ~(uint64_t)3;
     b = b < lim ? b : lim;
     e = e < lim ? e : lim;
-    e = e > b ? e : b;
-    rd.start(a.streams, b, e);
-#pragma unroll
-    for (int i = 0; i < 5; ++i) code = (code << 8) | rd.byte();
+    if (e < b + 4) {   // not a stream (corrupt offsets): decode the buffer's first dword
+      b = 0;
+      e = 4;
+    }
+    code = rd.start(reinterpret_cast<const uint32_t*>(a.streams + b), (uint32_t)((e - b) >> 2));
   }
 
   const int64_t tab0 = (int64_t)lk * a.C * 2;
@@ -130,13 +149,18 @@ __global__ __launch_bounds__(kMaxThreads) void codec_decode_kernel(CodecArgs a) 
     const uint64_t base = a.tab_off[ti0];
     if (tid < 2 * cb) {
       const int64_t ti = ti0 + tid;
-      s_first[tid] = a.tab_first[ti];
+      const int first = min(max(a.tab_first[ti], -128), 383);
       const int n = min(max(a.tab_n[ti], 1), 256);
       const uint64_t off = a.tab_off[ti];
       uint64_t lo = off >= base ? off - base : 0;
       lo = lo + n <= (uint64_t)kTabEntries ? lo : (uint64_t)(kTabEntries - n);
-      s_loff[tid] = (int)lo;
-      s_n[tid] = n;
+      s_meta[tid] = (uint32_t)lo | ((uint32_t)(n - 1) << 14) | ((uint32_t)(first + 128) << 22);
+    }
+    if (tid < cb) {
+      const int n0 = min(max(a.tab_n[ti0 + 2 * tid], 1), 256) - 1;
+      const int n1 = min(max(a.tab_n[ti0 + 2 * tid + 1], 1), 256) - 1;
+      const uint32_t k0 = n0 ? 32 - __builtin_clz(n0) : 0, k1 = n1 ? 32 - __builtin_clz(n1) : 0;
+      s_steps[tid] = k0 | (k1 << 4) | (max(k0, k1) << 8);
     }
     if (tid < cb) {
       s_lo[tid] = a.lo[(int64_t)lk * a.C + cg + tid];
@@ -155,36 +179,39 @@ __global__ __launch_bounds__(kMaxThreads) void codec_decode_kernel(CodecArgs a) 
       const int kind = anchor ? 0 : 1;
       uint32_t word = 0;
       for (int j = 0; j < cb; ++j) {
-        const int ti = 2 * j + kind;
-        const int n = s_n[ti], lo_off = s_loff[ti];
+        const uint32_t meta = s_meta[2 * j + kind];
+        const int lo_off = meta & 0x3fff, last = (meta >> 14) & 0xff;
+        const int first = (int)(meta >> 22) - 128;
+        // slice index floor(code / r): a float estimate, off by at most one,
+        // corrected with the 32-bit remainder (|remainder| < 2 r <= 2^17)
         uint32_t r = rng >> 16;
         r = r ? r : 1u;
         uint32_t q = (uint32_t)((float)code * __builtin_amdgcn_rcpf((float)r));
-        int64_t rem = (int64_t)code - (int64_t)q * r;
-        if (rem < 0) {
-          --q;
-        } else if (rem >= (int64_t)r) {
-          ++q;
-        }
+        const uint32_t rem = code - q * r;
+        q = (int32_t)rem < 0 ? q - 1 : (rem >= r ? q + 1 : q);
         const uint32_t v = q < 65535u ? q : 65535u;
-        int x = 0, y = n - 1;
-        while (x < y) {
-          const int m = (x + y + 1) >> 1;
-          if (s_cdf[lo_off + m] <= v) x = m; else y = m - 1;
+        // largest x <= last with cdf[x] <= v (cdf[0] = 0): binary lifting over
+        // the wave's step count, a compare and a select per step
+        const int steps = __builtin_amdgcn_readfirstlane((s_steps[j] >> step_shift) & 0xf);
+        int x = 0;
+        for (int k = steps - 1; k >= 0; --k) {
+          const int m = x + (1 << k);
+          const uint32_t c = s_cdf[lo_off + min(m, last)];
+          x = (m <= last) & (c <= v) ? m : x;
         }
         const uint32_t c_lo = s_cdf[lo_off + x];
-        const uint32_t c_hi = x + 1 < n ? s_cdf[lo_off + x + 1] : 65536u;
+        const uint32_t c_hi = x < last ? s_cdf[lo_off + x + 1] : 65536u;
         code -= r * c_lo;
         rng = r * (c_hi > c_lo ? c_hi - c_lo : 1u);
-        if (rng < (1u << 24)) {
-          rng <<= 8;
-          code = (code << 8) | rd.byte();
-          if (rng < (1u << 24)) {
-            rng <<= 8;
-            code = (code << 8) | rd.byte();
-          }
-        }
-        word |= (uint32_t)((s_first[ti] + x) & 0xff) << (8 * (j & 3));
+        // renormalise: 0, 1 or 2 bytes, branch-free
+        const int nb = (rng < (1u << 24)) + (rng < (1u << 16));
+        const uint32_t top = (uint32_t)(rd.bits >> 48);            // next two bytes
+        code = (code << (8 * nb)) | (top >> (16 - 8 * nb));
+        rng <<= 8 * nb;
+        rd.bits <<= 8 * nb;
+        rd.avail -= 8 * nb;
+        rd.refill();
+        word |= (uint32_t)((first + x) & 0xff) << (8 * (j & 3));
         if ((j & 3) == 3 || j == cb - 1) {
           s_tile[row * kRowDwords + (j >> 2)] = word;
           word = 0;
@@ -229,9 +256,15 @@ __global__ __launch_bounds__(kMaxThreads) void codec_decode_kernel(CodecArgs a) 
 
 }  // namespace
 
-// Token groups per workgroup for a group size: 64, or as many as 1024
-// threads hold.
-int codec_groups_per_block(int group) { return group <= 16 ? 64 : kMaxThreads / group; }
+// Token groups per workgroup: at most 64 (or as many as 1024 threads hold),
+// spread evenly over the workgroups a slice's T tokens need, so the last
+// workgroup is not left mostly empty.
+int codec_groups_per_block(int group, int T) {
+  const int cap = group <= 16 ? 64 : kMaxThreads / group;
+  const int groups = (T + group - 1) / group;
+  const int blocks = (groups + cap - 1) / cap;
+  return (groups + blocks - 1) / blocks;
+}
 
 hipError_t launch_codec_decode(const kvs_codec_layout& lay, const kvs_codec_chunk& ch, void* out,
                                hipStream_t s) {
@@ -252,13 +285,14 @@ hipError_t launch_codec_decode(const kvs_codec_layout& lay, const kvs_codec_chun
   a.C = lay.C;
   a.group = lay.group;
   a.S = lay.S;
-  a.NG = codec_groups_per_block(lay.group);
+  a.NG = codec_groups_per_block(lay.group, lay.T);
   for (int i = 0; i < 3; ++i) a.bins[i] = lay.bins[i];
   const int TB = a.NG * a.group;
   const int threads = (TB + 63) / 64 * 64;
   const dim3 grid((unsigned)((lay.T + TB - 1) / TB), (unsigned)(lay.C / lay.S),
                   (unsigned)(lay.L * 2));
-  hipLaunchKernelGGL(codec_decode_kernel, grid, dim3((unsigned)threads), 0, s, a);
+  const size_t tile = (size_t)TB * kRowDwords * sizeof(uint32_t);
+  hipLaunchKernelGGL(codec_decode_kernel, grid, dim3((unsigned)threads), tile, s, a);
   return hipGetLastError();
 }
 
