@@ -293,13 +293,18 @@ def tier_report(name: str = "flexicache_topk", period: int = 16, windows: int = 
     torch.cuda.empty_cache()
 
     res = {}
-    for mode in ("tiered", "resident"):
-        loop = TieredLoop(wl, steps, period=period, tiered=mode == "tiered", stable=stable)
+    for mode in ("tiered", "resident", "tiered_append", "resident_append"):
+        loop = TieredLoop(wl, steps, period=period, tiered=mode.startswith("tiered"),
+                          stable=stable, append=mode.endswith("append"))
         if mode == "tiered":
             gpu_b, full_b = loop.gpu_bytes, loop.full_bytes
         prom = []
         for t in range(steps):
-            if mode == "tiered" and t % period == 0:
+            if mode.startswith("tiered") and t % period == 0:
+                if loop.append:
+                    for l in range(c.L):
+                        k, v = loop.kv[t][l]
+                        kvs.kvs_append_kv_tier(loop.ds.caches[l], loop.tiers[l], k, v)
                 due = [loop.select(t, l) for l in range(c.L)]
                 torch.cuda.synchronize()
                 ms = timed(lambda: [loop.promote(l, due[l]) for l in range(c.L)])
@@ -341,10 +346,10 @@ def tier_report(name: str = "flexicache_topk", period: int = 16, windows: int = 
         "promotion": reranks,
         "promotion_later_reranks_GBps": round(statistics.mean([r["GBps"] for r in later]), 2)
         if later else None,
-        "us_per_step": {"tiered": round(res["tiered"]["us_per_step"], 1),
-                        "resident": round(res["resident"]["us_per_step"], 1)},
+        "us_per_step": {m: round(res[m]["us_per_step"], 1) for m in res},
         "window": f"steps 0..{steps - 2} as one graph: {windows} reranks with promotion, the "
-                  "other steps scoring only unstable heads",
+                  "other steps scoring only unstable heads; *_append: each step first appends "
+                  "its token (written through to the host pages when tiered)",
     }
 
 

@@ -79,8 +79,8 @@ enum { KVS_F16 = 0, KVS_BF16 = 1 };
  * A group is allocated pages for its longest head [T 3.2]; shorter heads of
  * the group leave the tail of their slots unused.
  *
- *   kv          device, [num_pages][Hp][2][P][d] dtype.  Written only by
- *               kvs_append_kv.
+ *   kv          device, [num_pages][Hp][2][P][d] dtype.  Written by the
+ *               appends and kvs_promote_pages.
  *   minmax      device, [num_meta][d][2] dtype: the min-max cache [F Key
  *               observations, assumption 2], kept apart from the KV pages
  *               and ragged per head: block meta_base[r][h] + p holds, for
@@ -99,7 +99,8 @@ enum { KVS_F16 = 0, KVS_BF16 = 1 };
  *   seq_len     device, [b][Hkv] int32: n, the tokens head h of request r
  *               holds (ceil(B*N) retained under Budget Reservation [T 3.1],
  *               plus the tokens appended since), 1 <= n <= P*max_group_pages.
- *               Written only by kvs_append_kv.
+ *               Written only by the appends (kvs_append_kv,
+ *               kvs_append_kv_tier) and kvs_prefill_chunk.
  *   head_slot   device, [Hkv] int32: head h sits in group head_slot[h]/Hp,
  *               slot head_slot[h]%Hp; a permutation of [0, Hkv).
  *   b, Hq, Hkv  requests, query heads, KV heads (Hq % Hkv == 0).
@@ -279,6 +280,20 @@ typedef struct kvs_host_tier {
  * pages outside [0, num_host_pages) are skipped.  Needs b*Hkv <= 65535.
  */
 int kvs_offload_pages(const kvs_paged_kv* cache, const kvs_host_tier* tier, void* stream);
+
+/*
+ * kvs_append_kv on a cache with a host tier [F tiered placement: a stable
+ * head's pages, newly filled ones included, live in host memory].  For a
+ * tiered head the K and V rows are written through to host page
+ * host_base[r][h] + n/P (row n%P), and also to the GPU page when the table
+ * maps that page; its bounds are merged and n advances as in kvs_append_kv.
+ * The host copy of every page thus stays complete, and a later promotion
+ * brings the new rows along.  A tiered head whose host page is outside
+ * [0, num_host_pages) is skipped (n unchanged).  Other heads: kvs_append_kv.
+ * Reads only host_kv, host_base and num_host_pages of the tier.
+ */
+int kvs_append_kv_tier(const kvs_paged_kv* cache, const kvs_host_tier* tier, const void* k_new,
+                       const void* v_new, void* stream);
 
 /*
  * Promotion after a rerank [F tiered placement; physical block reuse in the

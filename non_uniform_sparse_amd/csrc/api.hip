@@ -232,7 +232,8 @@ extern "C" int kvs_append_kv(const kvs_paged_kv* cache, const void* k_new, const
   if (!k_new || !v_new) return set_error(KVS_EINVAL, "%s: null k_new or v_new", fn);
   if (!aligned16(k_new) || !aligned16(v_new))
     return set_error(KVS_EINVAL, "%s: k_new and v_new must be 16-byte aligned", fn);
-  if (hipError_t e = launch_append(c, k_new, v_new, (hipStream_t)stream)) return hip_error(e, fn);
+  if (hipError_t e = launch_append(c, nullptr, k_new, v_new, (hipStream_t)stream))
+    return hip_error(e, fn);
   return KVS_OK;
 }
 
@@ -304,6 +305,22 @@ extern "C" int kvs_offload_pages(const kvs_paged_kv* cache, const kvs_host_tier*
   HostTierView t;
   if (int rc = map_tier(tier, fn, &t)) return rc;
   if (hipError_t e = launch_offload(c, t, (hipStream_t)stream)) return hip_error(e, fn);
+  return KVS_OK;
+}
+
+extern "C" int kvs_append_kv_tier(const kvs_paged_kv* cache, const kvs_host_tier* tier,
+                                  const void* k_new, const void* v_new, void* stream) {
+  clear_error();
+  static const char* fn = "kvs_append_kv_tier";
+  CacheView c;
+  if (int rc = check_cache(cache, true, fn, &c)) return rc;
+  if (!k_new || !v_new) return set_error(KVS_EINVAL, "%s: null k_new or v_new", fn);
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return set_error(KVS_EINVAL, "%s: k_new and v_new must be 16-byte aligned", fn);
+  if (int rc = check_tier_fields(tier, c, fn)) return rc;
+  HostTierView t;
+  if (int rc = map_tier(tier, fn, &t)) return rc;
+  if (hipError_t e = launch_append(c, &t, k_new, v_new, (hipStream_t)stream)) return hip_error(e, fn);
   return KVS_OK;
 }
 

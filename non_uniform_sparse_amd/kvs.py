@@ -27,7 +27,7 @@ KVS_PAGE_ON_HOST = -2
 EXPORTS = (
     "kvs_build_minmax", "kvs_score_pages", "kvs_score_pages_heads", "kvs_topk_pages",
     "kvs_topk_pages_heads", "kvs_append_kv", "kvs_prefill_chunk", "kvs_prefill_workspace_bytes",
-    "kvs_offload_pages", "kvs_promote_pages",
+    "kvs_offload_pages", "kvs_promote_pages", "kvs_append_kv_tier",
     "kvs_codec_bounds", "kvs_codec_encode", "kvs_codec_decode",
     "kvs_plan_split",
     "kvs_decode_attn",
@@ -118,6 +118,7 @@ def lib() -> ctypes.CDLL:
         ptier = ctypes.POINTER(HostTier)
         L.kvs_offload_pages.argtypes = [pkv, ptier, vp]
         L.kvs_promote_pages.argtypes = [pkv, ptier, vp, vp, i32, vp, vp, vp]
+        L.kvs_append_kv_tier.argtypes = [pkv, ptier, vp, vp, vp]
         play, pch = ctypes.POINTER(CodecLayout), ctypes.POINTER(CodecChunk)
         L.kvs_codec_bounds.argtypes = [play, ctypes.POINTER(ctypes.c_uint64),
                                        ctypes.POINTER(ctypes.c_uint64)]
@@ -294,6 +295,18 @@ def kvs_offload_pages(cache: Cache, tier: Tier, stream=None) -> None:
     """Copy every resident page of the tiered heads to its host page."""
     s, t = cache.struct(), tier.struct(cache)
     _check(lib().kvs_offload_pages(ctypes.byref(s), ctypes.byref(t), _stream(stream)))
+
+
+def kvs_append_kv_tier(cache: Cache, tier: Tier, k_new: torch.Tensor, v_new: torch.Tensor,
+                       stream=None) -> None:
+    """kvs_append_kv with the tiered heads' rows written through to their
+    host pages."""
+    s, t = cache.struct(), tier.struct(cache)
+    dev = cache.kv.device
+    _need(k_new, "k_new", (s.b, s.Hkv, s.d), cache.kv.dtype, dev)
+    _need(v_new, "v_new", (s.b, s.Hkv, s.d), cache.kv.dtype, dev)
+    _check(lib().kvs_append_kv_tier(ctypes.byref(s), ctypes.byref(t), _ptr(k_new), _ptr(v_new),
+                                    _stream(stream)))
 
 
 def kvs_promote_pages(cache: Cache, tier: Tier, sel: torch.Tensor, sel_count: torch.Tensor,

@@ -43,7 +43,8 @@ def heads_due(t: int, stable: np.ndarray, period: int) -> np.ndarray:
 
 class DecodeLoop:
     def __init__(self, wl: Workload, steps: int, device="cuda", period: int = 16,
-                 unstable_frac: float = 0.25, T: Optional[int] = None, poison: bool = True):
+                 unstable_frac: float = 0.25, T: Optional[int] = None, poison: bool = True,
+                 stable: Optional[np.ndarray] = None):
         c = wl.cfg
         if not c.topk:
             raise ValueError("the rerank schedule needs a top-K workload")
@@ -55,7 +56,8 @@ class DecodeLoop:
         self.wl, self.cfg, self.device = wl, c, device
         self.steps, self.period = steps, period
         self.ds = DecodeStep(wl, device=device, T=T, poison=poison, growth=steps)
-        self.stable = wl.stable_heads(unstable_frac)            # [L][Hkv]
+        self.stable = (wl.stable_heads(unstable_frac) if stable is None
+                       else np.array(stable, dtype=bool))       # [L][Hkv]
         self.n0 = [cache.seq_len.clone() for cache in self.ds.caches]
         # every step's inputs, resident on the device before any step runs
         self.q = [[wl.step_q(t, l, device) for l in range(c.L)] for t in range(steps)]

@@ -16,11 +16,13 @@ in bulk (``kvs_offload_pages``), then the GPU pool is compacted to the
 unstable heads' pages plus the stable heads' slots -- a host-side
 re-layout, like the rest of the allocator in layout.py.
 
-The decode runs on a fixed cache (no tokens appended; see ``steps.py`` for
-appends): the rerank schedule of ``steps.heads_due`` decides which heads
-re-select, and the heads that re-select promote.  The same schedule on the
-fully resident cache (``tiered=False``) gives the same selections and,
-because the decode reads only selected pages, the same outputs bit for bit.
+Each step runs the rerank schedule of ``steps.heads_due``: the heads due
+re-select, and the tiered ones among them promote.  With ``append=True`` the
+step first appends its token, written through to the tiered heads' host
+pages (``kvs_append_kv_tier``), so the host copy of every page, newly filled
+ones included, stays complete.  The same schedule on the fully resident
+cache gives the same selections and, because the decode reads only selected
+pages, the same outputs bit for bit.
 """
 
 from __future__ import annotations
@@ -65,18 +67,23 @@ def build_tier(cache: Cache, stable: np.ndarray, slots: int, seed: int = 99):
     b, Hkv = cache.seq_len.shape
     maxpg = cache.page_table.shape[2]
     pt = cache.page_table.cpu().numpy()
-    seq = cache.seq_len.cpu().numpy().astype(np.int64)
     hs = cache.head_slot.cpu().numpy()
-    npg = -(-seq // P)
     tiered = np.broadcast_to(np.asarray(stable, dtype=bool)[None, :], (b, Hkv))
 
+    # every mapped page of a tiered head gets a host page, the pages mapped
+    # for tokens still to be appended included
+    mapped = np.zeros((b, Hkv), dtype=np.int64)
+    for r in range(b):
+        for h in range(Hkv):
+            got = np.nonzero(pt[r, hs[h]] >= 0)[0]
+            mapped[r, h] = int(got[-1]) + 1 if got.size else 0
     host_base = np.full((b, Hkv), -1, dtype=np.int64)
     run = 0
     for r in range(b):
         for h in range(Hkv):
             if tiered[r, h]:
                 host_base[r, h] = run
-                run += int(npg[r, h])
+                run += int(mapped[r, h])
     host_kv = torch.empty((max(1, run), 2, P, d), dtype=dt, pin_memory=True)
     hb_dev = torch.from_numpy(host_base).to(dev)
     scratch = torch.full((b, Hkv, slots), -1, dtype=torch.int32, device=dev)
@@ -108,8 +115,8 @@ def build_tier(cache: Cache, stable: np.ndarray, slots: int, seed: int = 99):
                 slot_phys[r, h] = ids[k:k + slots]
                 k += slots
                 row = pt[r, hs[h]]
-                on_host = row[:npg[r, h]] >= 0
-                new_pt[r, hs[h], :npg[r, h]][on_host] = KVS_PAGE_ON_HOST
+                m = int(mapped[r, h])
+                new_pt[r, hs[h], :m][row[:m] >= 0] = KVS_PAGE_ON_HOST
 
     kv = torch.empty((max(1, total), 1, 2, P, d), dtype=dt, device=dev)
     kv.view(torch.int16).fill_(0x7E00 if dt == torch.float16 else 0x7FC0)   # NaN: unread slots
@@ -132,7 +139,8 @@ class TieredLoop:
 
     def __init__(self, wl: Workload, steps: int, device="cuda", period: int = 16,
                  unstable_frac: float = 0.25, slots: Optional[int] = None, tiered: bool = True,
-                 T: Optional[int] = None, stable: Optional[np.ndarray] = None):
+                 T: Optional[int] = None, stable: Optional[np.ndarray] = None,
+                 append: bool = False):
         c = wl.cfg
         if not c.topk:
             raise ValueError("tiered placement needs a top-K workload")
@@ -143,9 +151,9 @@ class TieredLoop:
         if period < 1 or steps < 1:
             raise ValueError("steps >= 1 and period >= 1 required")
         self.wl, self.cfg, self.device = wl, c, device
-        self.steps, self.period, self.tiered = steps, period, tiered
+        self.steps, self.period, self.tiered, self.append = steps, period, tiered, append
         self.slots = c.topk if slots is None else int(slots)
-        self.ds = DecodeStep(wl, device=device, T=T, poison=True)
+        self.ds = DecodeStep(wl, device=device, T=T, poison=True, growth=steps if append else 0)
         self.stable = (wl.stable_heads(unstable_frac) if stable is None
                        else np.asarray(stable, dtype=bool))            # [L][Hkv]
         self.full_bytes = sum(cc.kv.numel() * cc.kv.element_size() for cc in self.ds.caches)
@@ -159,9 +167,12 @@ class TieredLoop:
             torch.cuda.synchronize()
         self.gpu_bytes = sum(cc.kv.numel() * cc.kv.element_size() for cc in self.ds.caches)
         self.pt0 = [cc.page_table.clone() for cc in self.ds.caches]
+        self.n0 = [cc.seq_len.clone() for cc in self.ds.caches]
         self.moved = [torch.zeros((c.b, c.Hkv), dtype=torch.int32, device=device)
                       for _ in range(c.L)]
         self.q = [[wl.step_q(t, l, device) for l in range(c.L)] for t in range(steps)]
+        self.kv = ([[wl.step_kv(t, l, device) for l in range(c.L)] for t in range(steps)]
+                   if append else None)
 
     def heads_due(self, t: int, l: int) -> np.ndarray:
         return heads_due(t, self.stable[l], self.period)
@@ -188,6 +199,12 @@ class TieredLoop:
                                   moved=self.moved[l], stream=stream)
 
     def run_layer(self, t: int, l: int, stream=None) -> torch.Tensor:
+        if self.append:
+            k, v = self.kv[t][l]
+            if self.tiered:
+                kvs.kvs_append_kv_tier(self.ds.caches[l], self.tiers[l], k, v, stream)
+            else:
+                kvs.kvs_append_kv(self.ds.caches[l], k, v, stream)
         due = self.select(t, l, stream)
         self.promote(l, due, stream)
         return self.ds.attend(l, self.q[t][l], stream)
@@ -197,9 +214,12 @@ class TieredLoop:
             self.run_layer(t, l, stream)
 
     def rewind(self) -> None:
-        """Back to the state before step 0: no stable-head page resident."""
+        """Back to the state before step 0: no stable-head page resident and,
+        with appends, the tokens each head held when the caches were built
+        (re-running the steps rewrites the same rows and bounds)."""
         for l in range(self.cfg.L):
             self.ds.caches[l].page_table.copy_(self.pt0[l])
+            self.ds.caches[l].seq_len.copy_(self.n0[l])
             if self.tiers[l] is not None:
                 self.tiers[l].slot_page.fill_(-1)
 

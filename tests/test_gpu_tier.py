@@ -232,3 +232,94 @@ def test_tier_full_size_sampled():
     frac = tl.moved[0].sum().item()
     say(f"tier full size: GPU KV {tl.gpu_bytes / 2**30:.2f} GiB of {ref.full_bytes / 2**30:.2f} "
         f"GiB; pages moved on the last rerank {frac}")
+
+
+@pytest.mark.parametrize("name,ov,steps,period", [
+    ("flexicache_topk", dict(b=3, N=2000, Hp=1), 9, 4),
+    ("gemma3_mixed", dict(b=3, L=2, N=4096, topk=16, Hp=1), 7, 3),
+])
+def test_tier_with_appends_matches_resident(name, ov, steps, period):
+    """Decoding with appends on the tiered cache (rows written through to
+    the host pages) against the same steps on the fully resident cache
+    (DecodeLoop): lengths, bounds, selections and outputs equal bit for bit
+    at every step; every tiered head's host pages hold all its tokens, old
+    and appended; resident pages equal their host pages; the resident set is
+    the selection."""
+    from non_uniform_sparse_amd.steps import DecodeLoop
+    require_gpu()
+    wl = make_workload(name, **ov)
+    c = wl.cfg
+    say(f"[case] tier appends {name} {ov} steps={steps} period={period}")
+    stable = _stable(c)
+    tl = TieredLoop(wl, steps, period=period, stable=stable, append=True)
+    ref = DecodeLoop(wl, steps, period=period, stable=stable)
+    tokens = {}
+    for l in range(c.L):
+        for r in range(c.b):
+            for h in range(c.Hkv):
+                K, V = wl.head_kv(r, l, h, int(tl.ds.head_slot[l, h]), device="cuda")
+                tokens[(l, r, h)] = [_bits(K), _bits(V)]
+    for t in range(steps):
+        tl.run_step(t)
+        ref.run_step(t)
+        torch.cuda.synchronize()
+        for l in range(c.L):
+            a, b_ = tl.ds, ref.ds
+            assert torch.equal(a.caches[l].seq_len, b_.caches[l].seq_len)
+            assert torch.equal(a.caches[l].minmax.view(torch.int16), b_.caches[l].minmax.view(torch.int16))
+            assert torch.equal(a.bufs[l].sel, b_.bufs[l].sel) and torch.equal(a.bufs[l].sel_count,
+                                                                              b_.bufs[l].sel_count)
+            assert torch.equal(a.bufs[l].out, b_.bufs[l].out), f"output t={t} l={l}"
+            tier, lay = tl.tiers[l], tl.tier_layouts[l]
+            hk = _bits(tier.host_kv)
+            kvb = _bits(a.caches[l].kv)
+            pt = a.caches[l].page_table.cpu().numpy()
+            sp, sph = tier.slot_page.cpu().numpy(), tier.slot_phys.cpu().numpy()
+            sel, cnt = a.bufs[l].sel.cpu().numpy(), a.bufs[l].sel_count.cpu().numpy()
+            kt, vt = [_bits(x) for x in tl.kv[t][l]]
+            for r in range(c.b):
+                for h in range(c.Hkv):
+                    KV = tokens[(l, r, h)]
+                    KV[0] = np.vstack([KV[0], kt[r, h][None]])
+                    KV[1] = np.vstack([KV[1], vt[r, h][None]])
+                    hb = int(lay.host_base[r, h])
+                    if hb < 0:
+                        continue
+                    n = KV[0].shape[0]
+                    for p in range(-(-n // c.P)):
+                        m = min(c.P, n - p * c.P)
+                        assert np.array_equal(hk[hb + p, 0, :m], KV[0][p * c.P:p * c.P + m]), (t, l, r, h, p)
+                        assert np.array_equal(hk[hb + p, 1, :m], KV[1][p * c.P:p * c.P + m]), (t, l, r, h, p)
+                    res = sp[r, h][sp[r, h] >= 0]
+                    assert sorted(res.tolist()) == sorted(sel[r, h, :cnt[r, h]].tolist())
+                    row = pt[r, int(tl.ds.head_slot[l, h])]
+                    for j in np.nonzero(sp[r, h] >= 0)[0]:
+                        p, ph = int(sp[r, h, j]), int(sph[r, h, j])
+                        assert row[p] == ph and np.array_equal(kvb[ph, 0], hk[hb + p])
+    say(f"tier appends {name}: {steps} steps equal to the resident cache")
+
+
+def test_tier_appends_window_graph():
+    """A captured window with appends and promotions replays, from the
+    rewound state, to the eager result twice."""
+    require_gpu()
+    wl = make_workload("flexicache_topk", b=3, N=2000, Hp=1)
+    say("[case] tier appends window graph")
+    tl = TieredLoop(wl, 6, period=3, stable=_stable(wl.cfg), append=True)
+    tl.rewind()
+    for t in range(6):
+        tl.run_step(t)
+    torch.cuda.synchronize()
+    ref_out = [o.clone() for o in tl.outputs()]
+    ref_len = [cc.seq_len.clone() for cc in tl.ds.caches]
+    g = tl.capture(6)
+    for rep in range(2):
+        for o in tl.outputs():
+            o.fill_(float("nan"))
+        tl.rewind()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for l in range(wl.cfg.L):
+            assert torch.equal(tl.outputs()[l], ref_out[l]), f"replay {rep} layer {l}"
+            assert torch.equal(tl.ds.caches[l].seq_len, ref_len[l])
