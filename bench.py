@@ -644,6 +644,27 @@ def main() -> int:
             mm_marks.append((a, b_))
     stream.synchronize()
     mm_ms = [a.elapsed_time(b_) for a, b_ in mm_marks]
+    # The empirical ceiling of the decode's gather: the same K/V tiles of the
+    # attended pages read through the page table with no arithmetic
+    # (kvs_gather_probe), per layer behind a GPU spin.
+    sink = torch.empty(kvs.kvs_gather_probe_sink_words(c.d), dtype=torch.int32, device=dev)
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(int(cycles_per_ms * (2.0 + 0.1 * c.L)))
+        pr_marks = []
+        for l in range(c.L):
+            a, b_ = ev(), ev()
+            buf = step.bufs[l]
+            a.record(stream)
+            kvs.kvs_gather_probe(step.caches[l], buf.sel if c.topk else None,
+                                 buf.sel_count if c.topk else None, c.topk or 0, sink, stream)
+            b_.record(stream)
+            pr_marks.append((a, b_))
+    stream.synchronize()
+    pr_ms = statistics.mean(a.elapsed_time(b_) for a, b_ in pr_marks)
+    units = [int(step.bufs[l].sel_count.sum()) if c.topk else int((-(-wl.n[:, l, :] // c.P)).sum())
+             for l in range(c.L)]
+    pr_bytes = statistics.mean(units) * 2 * c.P * c.d * 2
+    pr_gbps = pr_bytes / (pr_ms * 1e-3) / 1e9
     t_plan = time.perf_counter()
     for _ in range(20):
         kvs.kvs_plan_split(wl.budgets, step.head_slot, c.Hp, 0.0, step.T)
@@ -662,6 +683,10 @@ def main() -> int:
         rows["a3_topk"] = dict(row(kern["topk"], "topk_launch"), bound="latency")
     rows["a4_plan"] = {"us_host": round(plan_us, 1), "note": f"S[{c.L}][{c.G}], host, ahead of time"}
     rows["a5_a6_decode_combine"] = row(kern["decode_attn"], "decode_launch")
+    rows["gather_probe"] = {"us": round(pr_ms * 1e3, 2), "bytes": int(pr_bytes),
+                            "GBps": round(pr_gbps, 1), "frac": round(pr_gbps / HBM_PEAK_GBPS, 4),
+                            "note": "the decode's K/V tiles read through the page table, no "
+                                    "arithmetic: the access pattern's empirical ceiling"}
     pct = lambda f: per_step[min(len(per_step) - 1, int(f * len(per_step)))]
     dec_ms = statistics.mean(kern["decode_attn"])
     dec_bytes = statistics.mean(a["decode_launch"] for a in ab)
@@ -703,6 +728,8 @@ def main() -> int:
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
+            "empirical_ceiling_GBps": round(pr_gbps, 1),
+            "frac_of_empirical_ceiling": round(achieved / pr_gbps, 4),
         },
         "wall_ms_per_step_incl_flush": round(wall_ms / args.steps, 4),
         "step_ms_p10_p50_p90": [round(pct(0.1), 4), round(statistics.median(per_step), 4),

@@ -375,6 +375,27 @@ size_t kvs_decode_workspace_bytes(int32_t b, int32_t Hq, int32_t Hkv, int32_t d,
 int kvs_decode_concurrency(int32_t device, int32_t d, int32_t gqa, int32_t dtype, int32_t* W);
 
 /*
+ * Read probe of the decode's gather, a measurement aid (the empirical HBM
+ * ceiling of the decode's access pattern): for every (r, h) and each unit
+ * the decode attends -- sel[r][h][0 .. sel_count) clamped to the head's
+ * pages as in kvs_decode_attn, or every page when sel is NULL -- it reads
+ * that page's whole K and V tile of head h through the page table, with no
+ * arithmetic.  The XOR of all 32-bit words read by a wave is written to one
+ * sink word per wave; sink words past the grid's waves are untouched.  A
+ * null page counts for nothing (its loads go to page 0 and are not folded).
+ * The XOR over the sink words therefore equals the XOR of every word of the
+ * attended tiles of mapped pages.
+ *   sink        device, sink_words >= kvs_gather_probe_sink_words(d)
+ *               (KVS_ENOSPC otherwise).
+ * Needs b*Hkv <= 16383.
+ */
+int kvs_gather_probe(const kvs_paged_kv* cache, const int32_t* sel, const int32_t* sel_count,
+                     int32_t K, uint32_t* sink, size_t sink_words, void* stream);
+
+/* Sink words kvs_gather_probe needs on the current device for head_dim d. */
+int kvs_gather_probe_sink_words(int32_t d, int32_t* words);
+
+/*
  * KV-cache codec [C 3, 7]: one chunk of T tokens of every layer,
  *     x[L][2][T][C] fp16 (index 1: 0 = K, 1 = V; C = all KV heads' channels
  *     of a token side by side),

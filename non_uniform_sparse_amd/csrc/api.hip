@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include "kvs_internal.h"
+#include "kvs_launch.h"
 
 namespace kvs {
 
@@ -234,6 +235,34 @@ extern "C" int kvs_append_kv(const kvs_paged_kv* cache, const void* k_new, const
     return set_error(KVS_EINVAL, "%s: k_new and v_new must be 16-byte aligned", fn);
   if (hipError_t e = launch_append(c, nullptr, k_new, v_new, (hipStream_t)stream))
     return hip_error(e, fn);
+  return KVS_OK;
+}
+
+extern "C" int kvs_gather_probe_sink_words(int32_t d, int32_t* words) {
+  clear_error();
+  if (!words || (d != 128 && d != 256))
+    return set_error(KVS_EINVAL, "kvs_gather_probe_sink_words: null output or head_dim not 128/256");
+  if (probe_sink_words(d, words))
+    return set_error(KVS_EHIP, "kvs_gather_probe_sink_words: occupancy query failed");
+  return KVS_OK;
+}
+
+extern "C" int kvs_gather_probe(const kvs_paged_kv* cache, const int32_t* sel,
+                                const int32_t* sel_count, int32_t K, uint32_t* sink,
+                                size_t sink_words, void* stream) {
+  clear_error();
+  static const char* fn = "kvs_gather_probe";
+  CacheView c;
+  if (int rc = check_cache(cache, false, fn, &c)) return rc;
+  if (!sink) return set_error(KVS_EINVAL, "%s: null sink", fn);
+  if ((sel == nullptr) != (sel_count == nullptr))
+    return set_error(KVS_EINVAL, "%s: sel and sel_count go together", fn);
+  if (sel && (K < 1 || K > kMaxK)) return set_error(KVS_EINVAL, "%s: K=%d not in [1, %d]", fn, K, kMaxK);
+  if ((int64_t)c.b * c.Hkv > kMaxScoreHeads)
+    return set_error(KVS_EUNSUPPORTED, "%s: b*Hkv > %d", fn, kMaxScoreHeads);
+  if (hipError_t e = launch_probe(c, sel, sel_count, K, sink, sink_words, (hipStream_t)stream))
+    return e == hipErrorInvalidValue ? set_error(KVS_ENOSPC, "%s: sink too small", fn)
+                                     : hip_error(e, fn);
   return KVS_OK;
 }
 

@@ -17,6 +17,7 @@
 // page's first; lanes [d/8, d/4) store the V row.  Lane 0 then advances n.
 // Every skip condition is uniform over the wave.
 #include "kvs_device.h"
+#include "kvs_launch.h"
 
 namespace kvs {
 namespace {

@@ -29,6 +29,7 @@
 #include <hip/hip_fp16.h>
 
 #include "kvs_internal.h"
+#include "kvs_launch.h"
 
 namespace kvs {
 namespace {

@@ -15,6 +15,7 @@
 #include <vector>
 
 #include "kvs_internal.h"
+#include "kvs_launch.h"
 
 namespace kvs {
 namespace {

@@ -1,5 +1,6 @@
-// Internal declarations of libkvs: validated argument bundles passed to the
-// kernel launchers, error reporting and the launchers themselves.
+// Internal declarations of libkvs shared by every kernel: limits, error
+// reporting, the validated cache descriptor, head sets and the decode's
+// argument bundle and launchers.  The other launchers are in kvs_launch.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -17,9 +18,6 @@ constexpr int kMaxTopkPages = 8192;
 constexpr int kMaxK = 1024;
 constexpr int kMaxSplitsPerRequest = 65536;
 constexpr int kMaxScoreHeads = 16383;
-constexpr int kMaxChunk = 8192;          // prefill chunk length (16-bit kept positions)
-constexpr int kMaxSlots = 1024;          // GPU pages per tiered head
-constexpr int kMaxTierPages = 8192;      // max_group_pages of a tiered cache (LDS bitmap)
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Records a message for kvs_last_error() and returns `code`.
@@ -47,17 +45,6 @@ struct HeadMask {
   }
 };
 
-// A validated kvs_host_tier; host_kv is the device address of the pinned
-// host pages.
-struct HostTierView {
-  void* host_kv;
-  const int64_t* host_base;
-  int32_t* slot_page;
-  const int32_t* slot_phys;
-  int slots;
-  int64_t num_host_pages;
-};
-
 struct DecodeArgs {
   CacheView c;
   const void* q;
@@ -76,28 +63,7 @@ struct DecodeArgs {
   int S_prefix[kMaxGroups + 1];
 };
 
-hipError_t launch_minmax(const CacheView& c, hipStream_t s);
-hipError_t launch_score(const CacheView& c, const void* q, float* scores, const HeadMask& heads,
-                        hipStream_t s);
-hipError_t launch_topk(const float* scores, const int32_t* seq_len, int P, int b, int Hkv,
-                       int max_pages, int K, const HeadMask& heads, int32_t* sel,
-                       int32_t* sel_count, hipStream_t s);
-hipError_t launch_append(const CacheView& c, const HostTierView* tier, const void* k_new,
-                         const void* v_new, hipStream_t s);
-hipError_t launch_prefill(const CacheView& c, const void* k_chunk, const void* v_chunk,
-                          const float* scores, const int32_t* quota, int C, void* ws,
-                          hipStream_t s);
-size_t prefill_workspace_bytes(int b, int Hkv, int C);
-hipError_t launch_offload(const CacheView& c, const HostTierView& t, hipStream_t s);
-hipError_t launch_promote(const CacheView& c, const HostTierView& t, const int32_t* sel,
-                          const int32_t* sel_count, int K, const HeadMask& heads, int32_t* moved,
-                          hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
-// KV-cache codec: layout validation (shared by the encoder and the decoder)
-// and the decode launch.
-int codec_check_layout(const kvs_codec_layout* p, const char* fn);
-hipError_t launch_codec_decode(const kvs_codec_layout& lay, const kvs_codec_chunk& ch, void* out,
-                               hipStream_t s);
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s);
 // Resident decode workgroups per compute unit for a kernel variant.
 hipError_t decode_blocks_per_cu(int d, int gqa, int dtype, int* blocks);

@@ -18,6 +18,7 @@
 // missing page reads page 0 and is discarded; indices are clamped into the
 // segment), which keeps the compiler's wait counting exact.
 #include "flat_pages.h"
+#include "kvs_launch.h"
 
 namespace kvs {
 namespace {

@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "kvs_internal.h"
+#include "kvs_launch.h"
 
 namespace {
 

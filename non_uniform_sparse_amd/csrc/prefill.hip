@@ -19,6 +19,7 @@
 // when it already had tokens before this chunk.  Every row's K and V is
 // read once and written once.
 #include "radix_select.h"
+#include "kvs_launch.h"
 
 namespace kvs {
 namespace {

@@ -26,6 +26,7 @@
 // from a final block-strided fill.  The butterfly order is fixed:
 // deterministic.
 #include "flat_pages.h"
+#include "kvs_launch.h"
 
 namespace kvs {
 namespace {

@@ -26,6 +26,7 @@
 // Writes in step 1 touch only unselected pages and step 2 reads only
 // selected ones, so the two never meet.
 #include "radix_select.h"
+#include "kvs_launch.h"
 
 namespace kvs {
 namespace {

@@ -6,6 +6,7 @@
 // the selection it holds.  Integer work only, so the result is
 // deterministic.
 #include "radix_select.h"
+#include "kvs_launch.h"
 
 namespace kvs {
 namespace {

@@ -29,6 +29,7 @@ EXPORTS = (
     "kvs_topk_pages_heads", "kvs_append_kv", "kvs_prefill_chunk", "kvs_prefill_workspace_bytes",
     "kvs_offload_pages", "kvs_promote_pages", "kvs_append_kv_tier",
     "kvs_codec_bounds", "kvs_codec_encode", "kvs_codec_decode",
+    "kvs_gather_probe", "kvs_gather_probe_sink_words",
     "kvs_plan_split",
     "kvs_decode_attn",
     "kvs_decode_workspace_bytes", "kvs_decode_concurrency", "kvs_cluster_heads",
@@ -124,6 +125,8 @@ def lib() -> ctypes.CDLL:
                                        ctypes.POINTER(ctypes.c_uint64)]
         L.kvs_codec_encode.argtypes = [play, vp, pch, i32]
         L.kvs_codec_decode.argtypes = [play, pch, vp, vp]
+        L.kvs_gather_probe.argtypes = [pkv, vp, vp, i32, vp, ctypes.c_size_t, vp]
+        L.kvs_gather_probe_sink_words.argtypes = [i32, ctypes.POINTER(i32)]
         L.kvs_plan_split.argtypes = [vp, vp, i32, i32, i32, f64, i32, vp]
         L.kvs_decode_attn.argtypes = [pkv, vp, vp, vp, i32, vp, f32, vp, ctypes.c_size_t, vp, vp]
         L.kvs_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, vp, i32]
@@ -403,6 +406,27 @@ def kvs_codec_decode(enc: Encoded, out: torch.Tensor, stream=None) -> None:
     _need(out, "out", (lay.L, 2, lay.T, lay.C), torch.float16, enc.streams.device)
     s = enc.struct()
     _check(lib().kvs_codec_decode(ctypes.byref(lay), ctypes.byref(s), _ptr(out), _stream(stream)))
+
+
+def kvs_gather_probe_sink_words(d: int) -> int:
+    w = ctypes.c_int32()
+    _check(lib().kvs_gather_probe_sink_words(d, ctypes.byref(w)))
+    return int(w.value)
+
+
+def kvs_gather_probe(cache: Cache, sel: Optional[torch.Tensor], sel_count: Optional[torch.Tensor],
+                     K: int, sink: torch.Tensor, stream=None) -> None:
+    """Read every attended K/V tile through the page table, no arithmetic
+    (the empirical ceiling of the decode's gather)."""
+    s = cache.struct()
+    dev = cache.kv.device
+    if sel is not None:
+        _need(sel, "sel", (s.b, s.Hkv, K), torch.int32, dev)
+        _need(sel_count, "sel_count", (s.b, s.Hkv), torch.int32, dev)
+    if sink.dtype != torch.int32 or not sink.is_contiguous() or sink.device != dev:
+        raise ValueError("sink: contiguous int32 on the cache's device")
+    _check(lib().kvs_gather_probe(ctypes.byref(s), _ptr(sel), _ptr(sel_count), K, _ptr(sink),
+                                  sink.numel(), _stream(stream)))
 
 
 def kvs_prefill_workspace_bytes(b: int, Hkv: int, C: int) -> int:
