@@ -90,11 +90,8 @@ class DecodeStep:
                     units = float((-(-wl.n // c.P)).sum(axis=2).mean())
                 T = splits_per_request(self.W, c.b, c.G, units)
             S = kvs.kvs_plan_split(wl.budgets, self.head_slot, c.Hp, topk_cap(wl), T)
-        self.S = np.asarray(S, dtype=np.int32)
-        self.T = int(self.S[0].sum())
         self.scale = 1.0 / math.sqrt(c.d)
-        ws = max(kvs.kvs_decode_workspace_bytes(c.b, c.Hq, c.Hkv, c.d, row) for row in self.S)
-        self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
+        self.set_splits(S, microbatches)
         self.bufs: List[LayerBuffers] = []
         for l in range(c.L):
             maxpg = self.layouts[l].page_table.shape[2]
@@ -106,7 +103,16 @@ class DecodeStep:
                 scores = sel = cnt = None
             out = torch.empty((c.b, c.Hq, c.d), dtype=torch.float32, device=device)
             self.bufs.append(LayerBuffers(scores, sel, cnt, out))
-        mb = max(1, min(int(microbatches), c.b))
+
+    def set_splits(self, S, microbatches: Optional[int] = None) -> None:
+        """Use the split map S [L][G] (T = its row sum per request) and size
+        the decode workspaces for it, whole-batch and per micro-batch."""
+        c, device = self.cfg, self.device
+        self.S = np.asarray(S, dtype=np.int32)
+        self.T = int(self.S[0].sum())
+        ws = max(kvs.kvs_decode_workspace_bytes(c.b, c.Hq, c.Hkv, c.d, row) for row in self.S)
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
+        mb = len(self.parts) if microbatches is None else max(1, min(int(microbatches), c.b))
         self.parts = [(c.b * k // mb, c.b * (k + 1) // mb) for k in range(mb)]
         self.part_ws = [
             torch.empty(max(kvs.kvs_decode_workspace_bytes(r1 - r0, c.Hq, c.Hkv, c.d, row)
