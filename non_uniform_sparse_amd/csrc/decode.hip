@@ -21,6 +21,7 @@
 // (d=256) K and V tiles stream in fully coalesced 16-byte accesses.  Logits
 // are pair-dots of q with K summed over the row's COLS lanes; p*V is
 // accumulated per lane and reduced over the row groups once per head.
+#include <algorithm>
 #include <utility>
 
 #include "decode_common.h"
@@ -297,19 +298,26 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   if (cur_j >= 0) end_head(cur_j);
 }
 
-// One wave per (request, query head).  The splits that touched the head form
-// the contiguous range [first, last] that the decode kernel recorded (an
-// empty split inside it carries lse = -inf).  M = max lse and the weights
-// 2^(lse - M) are formed lane-parallel (lane = split), then 8 splits are
-// merged per step: lane l takes split l / 8 of the step (its weight comes by
+// One workgroup of W = blockDim.x / 64 waves (1 to 4) per (request, query
+// head).  The splits that touched the head form the contiguous range
+// [first, last] that the decode kernel recorded (an empty split inside it
+// carries lse = -inf).  Every wave forms M = max lse over the whole range
+// (lane = split), then merges its own W-th of the range, 8 splits per step:
+// lane l takes split l / 8 of the step (its weight 2^(lse - M) comes by
 // shuffle) and channels (l % 8) * D/8 .. +D/8; the 8 split lanes of each
-// channel chunk are summed with DPP / lane swaps at the end.
+// channel chunk are summed with DPP / lane swaps.  The waves' sums meet in
+// LDS and are added in wave order, so the result does not depend on timing.
+// A head spanning hundreds of splits (long, full-budget heads) is thus not
+// one wave's serial walk.
 template <int D>
-__global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   constexpr int CH = D / 8;          // channels per lane
   constexpr int V4 = CH / 4;         // float4 loads per split row
+  __shared__ float s_acc[4][D];
+  __shared__ float s_den[4];
   const CacheView& c = a.c;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int W = blockDim.x >> 6;
   const int r = blockIdx.x / c.Hq;
   const int g = blockIdx.x % c.Hq;
   const int h = g / c.Gq;
@@ -324,25 +332,26 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a) {
   const int s_hi = cnt > 0 ? clampi(hi, s_lo, a.Smax - 1) : -1;
   const int64_t row = ((int64_t)r * c.Hq + g) * a.Smax;
 
-  float my_lse = -__builtin_inff(), M = -__builtin_inff();
+  float M = -__builtin_inff();
   for (int w0 = s_lo; w0 <= s_hi; w0 += 64) {
     const float v = w0 + lane <= s_hi ? a.lse_part[row + w0 + lane] : -__builtin_inff();
-    if (w0 == s_lo) my_lse = v;
     M = fmaxf(M, v);
   }
   M = group_max<64>(M);
+  // this wave's part of the range
+  const int per = (s_hi - s_lo + 1 + W - 1) / W;
+  const int w_lo = s_lo + wave * per, w_hi = min(s_hi, w_lo + per - 1);
   float acc[CH];
 #pragma unroll
   for (int e = 0; e < CH; ++e) acc[e] = 0.f;
   float den = 0.f;
   const int sl = lane / 8, dc = lane % 8;
   if (M > -__builtin_inff()) {
-    for (int w0 = s_lo; w0 <= s_hi; w0 += 64) {
-      const float lw = w0 == s_lo ? my_lse
-                                  : (w0 + lane <= s_hi ? a.lse_part[row + w0 + lane] : -__builtin_inff());
+    for (int w0 = w_lo; w0 <= w_hi; w0 += 64) {
+      const float lw = w0 + lane <= w_hi ? a.lse_part[row + w0 + lane] : -__builtin_inff();
       const float wt = __builtin_amdgcn_exp2f(lw - M);   // 0 for an empty split
       den += wt;
-      const int nsp = min(64, s_hi - w0 + 1);
+      const int nsp = min(64, w_hi - w0 + 1);
 #pragma unroll 2
       for (int s8 = 0; s8 < nsp; s8 += 8) {
         const int sp = s8 + sl;
@@ -371,13 +380,35 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a) {
     v = across_sum<16>(v);
     acc[e] = v;
   }
-  if (sl == 0) {
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    float4* o4 = reinterpret_cast<float4*>(dst + dc * CH);
+  if (W == 1) {   // one wave: its sums are the head's (uniform over the block)
+    if (sl == 0) {
+      const float inv = den > 0.f ? 1.f / den : 0.f;
+      float4* o4 = reinterpret_cast<float4*>(dst + dc * CH);
 #pragma unroll
-    for (int v = 0; v < V4; ++v)
-      o4[v] = make_float4(acc[4 * v] * inv, acc[4 * v + 1] * inv, acc[4 * v + 2] * inv,
-                          acc[4 * v + 3] * inv);
+      for (int v = 0; v < V4; ++v)
+        o4[v] = make_float4(acc[4 * v] * inv, acc[4 * v + 1] * inv, acc[4 * v + 2] * inv,
+                            acc[4 * v + 3] * inv);
+    }
+    return;
+  }
+  if (sl == 0) {
+#pragma unroll
+    for (int e = 0; e < CH; ++e) s_acc[wave][dc * CH + e] = acc[e];
+  }
+  if (lane == 0) s_den[wave] = den;
+  __syncthreads();
+  // wave 0 adds the waves' sums in wave order, D / 64 channels per lane
+  if (wave == 0) {
+    float dsum = 0.f;
+    for (int w = 0; w < W; ++w) dsum += s_den[w];
+    const float inv = dsum > 0.f ? 1.f / dsum : 0.f;
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) {
+      const int ch = lane + 64 * k;
+      float x = 0.f;
+      for (int w = 0; w < W; ++w) x += s_acc[w][ch];
+      dst[ch] = x * inv;
+    }
   }
 }
 
@@ -423,10 +454,13 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s) {
   const int64_t blocks = (int64_t)a.c.b * a.c.Hq;
+  // one wave per 128 splits a head can span (a group's splits, plus one on
+  // either side), at most 4
+  const int waves = std::min(4, std::max(1, (a.Smax + 2 + 127) / 128));
   if (a.c.d == 128)
-    hipLaunchKernelGGL((combine_kernel<128>), dim3((unsigned)blocks), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((combine_kernel<128>), dim3((unsigned)blocks), dim3(64 * waves), 0, s, a);
   else
-    hipLaunchKernelGGL((combine_kernel<256>), dim3((unsigned)blocks), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((combine_kernel<256>), dim3((unsigned)blocks), dim3(64 * waves), 0, s, a);
   return hipGetLastError();
 }
 
