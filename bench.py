@@ -397,6 +397,20 @@ def codec_report(name: str = "llama7b_chunk", reps: int = 10) -> dict:
             best = min(best, a.elapsed_time(b_))
         return best
 
+    # pipelined loading (transfer of chunk i overlapping the decode of chunk
+    # i - 1): the chunk, pinned once, loaded 4 times into two alternating outputs
+    pinned = codec.pin(enc)
+    loader = codec.PipelinedLoader(lay, enc.cdf.numel(), enc.streams.numel())
+    outs = [out, torch.empty_like(out)]
+    n_chunks = 4
+    loader.run([pinned] * 2, outs)
+    torch.cuda.synchronize()
+    a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    loader.run([pinned] * n_chunks, [outs[i % 2] for i in range(n_chunks)])
+    b_.record()
+    b_.synchronize()
+    pipe_ms = a.elapsed_time(b_) / n_chunks
     symbols = cfg.L * 2 * cfg.T * cfg.C
     return {
         "config": {"workload": name, "layers": cfg.L, "tokens": cfg.T, "channels": cfg.C,
@@ -410,6 +424,9 @@ def codec_report(name: str = "llama7b_chunk", reps: int = 10) -> dict:
         "decode_Gsymbols_per_s": round(symbols / (ms * 1e-3) / 1e9, 1),
         "h2d_encoded_us": round(h2d_ms(coded) * 1e3, 1),
         "h2d_raw_us": round(h2d_ms(raw) * 1e3, 1),
+        "pipelined_us_per_chunk": round(pipe_ms * 1e3, 1),
+        "pipelined": f"{n_chunks} chunks from pinned host memory, the copy of chunk i "
+                     "overlapping the decode of chunk i - 1 (two streams, two buffer sets)",
     }
 
 

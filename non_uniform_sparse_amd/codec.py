@@ -67,3 +67,60 @@ def make_chunk(cfg: ChunkConfig, device="cpu") -> torch.Tensor:
 
 def layout_of(cfg: ChunkConfig) -> kvs.CodecLayout:
     return kvs.codec_layout(cfg.L, cfg.T, cfg.C, cfg.group, cfg.S)
+
+
+_FIELDS = ("lo", "scale", "tab_first", "tab_n", "tab_off", "cdf", "streams", "stream_off")
+
+
+def pin(enc: kvs.Encoded) -> kvs.Encoded:
+    """The chunk's tensors in pinned host memory (so host-to-device copies run
+    asynchronously at the link's rate)."""
+    return kvs.Encoded(enc.layout, *[getattr(enc, f).pin_memory() for f in _FIELDS])
+
+
+class PipelinedLoader:
+    """Loads encoded chunks from pinned host memory and decodes them on the
+    GPU, the transfer of chunk i overlapping the decode of chunk i - 1
+    (CacheGen notes, 7).  Two device buffer sets alternate: the copy of chunk
+    i waits for the decode that last read its set, and the decode of chunk i
+    waits for its copy.  Both streams keep the default priority."""
+
+    def __init__(self, layout: kvs.CodecLayout, cdf_cap: int, streams_cap: int, device="cuda"):
+        L, T, C, S = layout.L, layout.T, layout.C, layout.S
+        nstreams = L * 2 * (C // S) * T
+        self.layout, self.device = layout, device
+        shapes = {"lo": ((L, 2, C), torch.float32), "scale": ((L, 2, C), torch.float32),
+                  "tab_first": ((L, 2, C, 2), torch.int32), "tab_n": ((L, 2, C, 2), torch.int32),
+                  "tab_off": ((L, 2, C, 2), torch.int32), "cdf": ((cdf_cap,), torch.int16),
+                  "streams": ((streams_cap,), torch.uint8),
+                  "stream_off": ((nstreams + 1,), torch.int64)}
+        self.sets = [{f: torch.empty(s, dtype=dt, device=device) for f, (s, dt) in shapes.items()}
+                     for _ in range(2)]
+        self.copy_stream = torch.cuda.Stream(device)
+
+    def run(self, chunks, outs) -> None:
+        """Decode chunks[i] (pinned host Encoded) into outs[i], in order, on
+        the current stream; returns once everything is queued."""
+        comp = torch.cuda.current_stream(self.device)
+        last_read = [None, None]
+        for i, enc in enumerate(chunks):
+            k = i % 2
+            buf = self.sets[k]
+            if enc.cdf.numel() > buf["cdf"].numel() or enc.streams.numel() > buf["streams"].numel():
+                raise ValueError("chunk larger than the loader's buffers")
+            with torch.cuda.stream(self.copy_stream):
+                if last_read[k] is not None:
+                    self.copy_stream.wait_event(last_read[k])
+                dev = {}
+                for f in _FIELDS:
+                    src = getattr(enc, f)
+                    dst = buf[f] if f not in ("cdf", "streams") else buf[f][:src.numel()]
+                    dst.copy_(src, non_blocking=True)
+                    dev[f] = dst
+                copied = torch.cuda.Event()
+                copied.record(self.copy_stream)
+            comp.wait_event(copied)
+            kvs.kvs_codec_decode(kvs.Encoded(enc.layout, **dev), outs[i], comp)
+            done = torch.cuda.Event()
+            done.record(comp)
+            last_read[k] = done

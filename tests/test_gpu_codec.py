@@ -118,3 +118,24 @@ def test_decode_full_size_and_deterministic():
     assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
     say(f"codec full size: {x.numel() * 2 / 2**20:.0f} MiB fp16 -> {enc.nbytes() / 2**20:.1f} MiB "
         f"({x.numel() * 2 / enc.nbytes():.2f}x)")
+
+
+def test_pipelined_loader_matches_separate_decodes():
+    """Chunks copied and decoded through the two-stream pipeline (transfer of
+    chunk i overlapping the decode of chunk i - 1) decode to exactly what
+    each chunk decodes to on its own -- more chunks than buffer sets, so the
+    sets are reused."""
+    require_gpu()
+    say("[case] codec pipelined loader")
+    cfgs = [codec.ChunkConfig("t", L=3, T=107, C=64, S=32, seed=i) for i in range(4)]
+    encs = [kvs.kvs_codec_encode(codec.layout_of(c), codec.make_chunk(c)) for c in cfgs]
+    want = [_decode(e) for e in encs]
+    cdf_cap = max(e.cdf.numel() for e in encs)
+    st_cap = max(e.streams.numel() for e in encs)
+    loader = codec.PipelinedLoader(codec.layout_of(cfgs[0]), cdf_cap, st_cap)
+    outs = [torch.full((3, 2, 107, 64), float("nan"), dtype=torch.float16, device="cuda")
+            for _ in encs]
+    loader.run([codec.pin(e) for e in encs], outs)
+    torch.cuda.synchronize()
+    for o, w in zip(outs, want):
+        assert np.array_equal(o.cpu().numpy().view(np.uint16), w.view(np.uint16))
