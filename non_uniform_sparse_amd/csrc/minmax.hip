@@ -10,7 +10,12 @@
 // tile is P = 16 rows of d contiguous elements; lane l reads 16 bytes (8
 // channels) of rows rg + RPL*k, rg = l / COLS, so each load instruction
 // covers RPL whole rows (1 KB).  Per-channel min/max over the lane's rows,
-// then across the RPL row groups with lane swaps.  The output is
+// then across the RPL row groups with lane swaps, taken on 16-bit order
+// keys rather than floats: flipping the sign bit of a non-negative value
+// and every bit of a negative one makes unsigned order equal float order,
+// so packed u16 min/max treat two channels per instruction with no
+// conversion, and the inverse map gives back the exact bits (-0 orders just
+// below +0; both are the same value).  The output is
 // channel-interleaved, (min, max) per channel, so that one page of one head
 // is a single contiguous 4*d-byte block, and goes to block meta_base[r][h] +
 // p of the min-max cache, not to the page's physical KV slot: each head's
@@ -22,6 +27,42 @@
 
 namespace kvs {
 namespace {
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+
+// Order keys of two fp16 / bf16 values, and their inverse.
+__device__ __forceinline__ uint32_t to_keys(uint32_t w) {
+  const uint32_t neg = __builtin_bit_cast(uint32_t, __builtin_bit_cast(i16x2, w) >> (short)15);
+  return w ^ (neg | 0x80008000u);
+}
+__device__ __forceinline__ uint32_t from_keys(uint32_t k) {
+  const uint32_t neg = __builtin_bit_cast(uint32_t, __builtin_bit_cast(i16x2, ~k) >> (short)15);
+  return k ^ ((neg & 0x7fff7fffu) | 0x80008000u);
+}
+__device__ __forceinline__ uint32_t kmin(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+__device__ __forceinline__ uint32_t kmax(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+// min / max of packed keys across lanes that differ in lane bits >= FROM
+// (FROM = 16 or 32)
+template <int FROM>
+__device__ __forceinline__ void across_keys(uint32_t& lo, uint32_t& hi) {
+  if (FROM == 16) {
+    const auto l = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto h = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    lo = kmin(l[0], l[1]);
+    hi = kmax(h[0], h[1]);
+  }
+  const auto l = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  const auto h = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  lo = kmin(l[0], l[1]);
+  hi = kmax(h[0], h[1]);
+}
 
 __device__ __forceinline__ int head_pages(const CacheView& c, int rh) {
   constexpr int P = 16;
@@ -79,44 +120,43 @@ __global__ __launch_bounds__(kFlatThreads) void minmax_kernel(CacheView c) {
         const int64_t meta = mb + p;
         if (phys < 0 || meta < 0 || meta > last_meta) return;
         const int valid = min(P, n - p * P);
-        float lo[8], hi[8];
+        uint32_t lo[4], hi[4];   // keys of channels (2e, 2e + 1) of the lane's 8
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          lo[e] = __builtin_inff();
-          hi[e] = -__builtin_inff();
+        for (int e = 0; e < 4; ++e) {
+          lo[e] = 0xffffffffu;
+          hi[e] = 0u;
         }
+        auto row = [&](const uint4& v) {
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int k = 0; k < TL; ++k) {
-          if (rg + RPL * k < valid) {
-            const uint32_t w[4] = {src[k].x, src[k].y, src[k].z, src[k].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float a = lo_f(w[e], DT()), b = hi_f(w[e], DT());
-              lo[2 * e] = fminf(lo[2 * e], a);
-              hi[2 * e] = fmaxf(hi[2 * e], a);
-              lo[2 * e + 1] = fminf(lo[2 * e + 1], b);
-              hi[2 * e + 1] = fmaxf(hi[2 * e + 1], b);
-            }
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t key = to_keys(w[e]);
+            lo[e] = kmin(lo[e], key);
+            hi[e] = kmax(hi[e], key);
           }
+        };
+        if (valid == P) {   // a full page (all but a head's last): no row masks
+#pragma unroll
+          for (int k = 0; k < TL; ++k) row(src[k]);
+        } else {
+#pragma unroll
+          for (int k = 0; k < TL; ++k)
+            if (rg + RPL * k < valid) row(src[k]);
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          lo[e] = -across_max<COLS>(-lo[e]);
-          hi[e] = across_max<COLS>(hi[e]);
-        }
+        for (int e = 0; e < 4; ++e) across_keys<COLS>(lo[e], hi[e]);
         if (rg == 0) {
+          // (min, max) of channel 2e from the low halves, of 2e + 1 from the high
+          uint32_t o[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t lb = from_keys(lo[e]), hb = from_keys(hi[e]);
+            o[2 * e] = __builtin_amdgcn_perm(hb, lb, 0x05040100u);
+            o[2 * e + 1] = __builtin_amdgcn_perm(hb, lb, 0x07060302u);
+          }
           uint16_t* mm = reinterpret_cast<uint16_t*>(c.minmax) + meta * 2 * D;
-          uint4 a, b;
-          a.x = pack2(lo[0], hi[0], DT());
-          a.y = pack2(lo[1], hi[1], DT());
-          a.z = pack2(lo[2], hi[2], DT());
-          a.w = pack2(lo[3], hi[3], DT());
-          b.x = pack2(lo[4], hi[4], DT());
-          b.y = pack2(lo[5], hi[5], DT());
-          b.z = pack2(lo[6], hi[6], DT());
-          b.w = pack2(lo[7], hi[7], DT());
-          *reinterpret_cast<uint4*>(mm + 16 * col) = a;
-          *reinterpret_cast<uint4*>(mm + 16 * col + 8) = b;
+          *reinterpret_cast<uint4*>(mm + 16 * col) = make_uint4(o[0], o[1], o[2], o[3]);
+          *reinterpret_cast<uint4*>(mm + 16 * col + 8) = make_uint4(o[4], o[5], o[6], o[7]);
         }
       };
       uint4 buf0[TL], buf1[TL];
