@@ -1,0 +1,75 @@
+"""Parity at the library's size limits, through the C ABI.
+
+The top-K keeps a head's scores in LDS, which caps a head at 8192 pages
+(131072 tokens) and K at 1024; both limits are taken here, with heavy
+score ties and -inf (null) pages in the top-K case, and end to end on a
+request whose heads reach the page limit (so one head spans thousands of
+units and its query rows merge hundreds of split partials)."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from gpu_harness import Stats, assert_output_bar, check_layer, require_gpu, say
+from non_uniform_sparse_amd import kvs
+from non_uniform_sparse_amd.pipeline import DecodeStep
+from non_uniform_sparse_amd.workloads import make_workload
+
+pytestmark = pytest.mark.gpu
+
+P = 16
+MAX_PAGES = 8192     # pages of one head the top-K takes
+MAX_K = 1024
+
+
+@pytest.mark.parametrize("K", [1, 1000, MAX_K])
+def test_topk_at_page_limit(K):
+    """Scores on a quarter grid (thousands of equal values per head) with 5%
+    -inf entries; page counts at the limit, one below it, a single page,
+    exactly K pages and one more.  Selection, count and -1 padding are exact
+    against the oracle's rule (largest first, equal scores to the lower
+    page, ascending output)."""
+    require_gpu()
+    say(f"[case] topk at the page limit K={K}")
+    g = np.random.default_rng(11)
+    b, Hkv = 2, 4
+    s = (np.round(g.standard_normal((b, Hkv, MAX_PAGES)) * 4) / 4).astype(np.float32)
+    s[g.random(s.shape) < 0.05] = -np.inf
+    n = np.array([[MAX_PAGES * P, MAX_PAGES * P - 5, 1, K * P],
+                  [(K + 1) * P, 17, (MAX_PAGES - 1) * P, 1000 * P + 3]], dtype=np.int32)
+    dev = "cuda"
+    scores = torch.from_numpy(s).to(dev)
+    seq = torch.from_numpy(n).to(dev)
+    sel = torch.full((b, Hkv, K), -7, dtype=torch.int32, device=dev)
+    cnt = torch.full((b, Hkv), -7, dtype=torch.int32, device=dev)
+    kvs.kvs_topk_pages(scores, seq, P, K, sel, cnt)
+    torch.cuda.synchronize()
+    sel_h, cnt_h = sel.cpu().numpy(), cnt.cpu().numpy()
+    for r in range(b):
+        for h in range(Hkv):
+            npg = -(-int(n[r, h]) // P)
+            want = O.topk_pages(s[r, h, :npg], K)
+            assert cnt_h[r, h] == len(want) == min(K, npg)
+            assert np.array_equal(sel_h[r, h, :len(want)], want), f"r={r} h={h}"
+            assert np.all(sel_h[r, h, len(want):] == -1)
+
+
+@pytest.mark.parametrize("topk", [None, MAX_K])
+def test_longest_heads_end_to_end(topk):
+    """One request whose heads hold 1 to 131072 tokens (8192 pages): min-max
+    build, scores, top-K with the largest K, split-K decode and combine, all
+    against the oracle."""
+    require_gpu()
+    wl = make_workload("llama8b_ragged", b=1, N=MAX_PAGES * P, Hq=16, d=128, dtype="bf16",
+                       Hp=2, topk=topk)
+    wl.n[0, 0, :] = [MAX_PAGES * P, MAX_PAGES * P - 1, 1, 17, 65537, 100000, 2, MAX_PAGES * P - P]
+    say(f"[case] longest heads topk={topk} n={wl.n[0, 0].tolist()}")
+    step = DecodeStep(wl, device="cuda")
+    assert step.layouts[0].page_table.shape[2] == MAX_PAGES
+    st = Stats()
+    check_layer(step, 0, step.queries()[0], [0], st)
+    assert st.minmax_checked == sum(-(-int(x) // P) for x in wl.n[0, 0])
+    assert_output_bar(st, f"longest heads topk={topk} S={step.S[0].tolist()}")
