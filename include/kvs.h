@@ -98,7 +98,9 @@ enum { KVS_F16 = 0, KVS_BF16 = 1 };
  *               only by kvs_promote_pages (tiered heads' entries).
  *   seq_len     device, [b][Hkv] int32: n, the tokens head h of request r
  *               holds (ceil(B*N) retained under Budget Reservation [T 3.1],
- *               plus the tokens appended since), 1 <= n <= P*max_group_pages.
+ *               plus the tokens appended since), 0 <= n <= P*max_group_pages
+ *               (n = 0: a head with no token yet, e.g. before the first
+ *               prefill chunk).
  *               Written only by the appends (kvs_append_kv,
  *               kvs_append_kv_tier) and kvs_prefill_chunk.
  *   head_slot   device, [Hkv] int32: head h sits in group head_slot[h]/Hp,
@@ -357,7 +359,10 @@ int kvs_plan_split(const double* budgets, const int32_t* head_slot, int32_t L, i
  *   scale      softmax scale, usually 1/sqrt(d).
  *   workspace  device scratch of at least kvs_decode_workspace_bytes(...)
  *              bytes, 256-byte aligned; contents on entry do not matter.
- *   out        device, [b][Hq][d] fp32.
+ *   out        device, [b][Hq][d] fp32.  A query head whose KV head has no
+ *              valid token in its attended pages (n = 0, an empty
+ *              selection, or only null pages) gets a zero row: attention
+ *              over no token is taken as the empty sum.
  */
 int kvs_decode_attn(const kvs_paged_kv* cache, const void* q, const int32_t* sel,
                     const int32_t* sel_count, int32_t K, const int32_t* S_row, float scale,

@@ -258,10 +258,14 @@ def attention_lse(q: np.ndarray, K: np.ndarray, V: np.ndarray,
 def lse_combine(parts: Sequence[Tuple[np.ndarray, float]]) -> Tuple[np.ndarray, float]:
     """Merge partial results of disjoint token sets: with M = max lse_s,
     o = sum exp(lse_s - M) o_s / sum exp(lse_s - M), lse = M + ln(sum ...).
-    Parts with lse = -inf (no tokens) carry no weight."""
+    Parts with lse = -inf (no tokens) carry no weight; when every part is
+    empty the merge is empty too, (0, -inf), as attention over no token is
+    (``attention_lse``)."""
+    if not parts:
+        raise ValueError("no part to merge")
     live = [(o, lse) for o, lse in parts if lse != -math.inf]
     if not live:
-        raise ValueError("no non-empty part")
+        return np.zeros_like(np.asarray(parts[0][0], dtype=np.float64)), -math.inf
     M = max(lse for _, lse in live)
     num = sum(math.exp(lse - M) * np.asarray(o, dtype=np.float64) for o, lse in live)
     den = sum(math.exp(lse - M) for _, lse in live)
@@ -299,7 +303,8 @@ def decode_group_split(q_slots: Sequence[np.ndarray], K_slots: Sequence[np.ndarr
     attended logical pages.  Split s processes its contiguous range of the
     head-major unit list; for every head it touches it produces a partial
     (o, lse) over that head's valid tokens in the range; the partials of each
-    query head are then merged with ``lse_combine``.  Returns [Gq][d] per slot.
+    query head are then merged with ``lse_combine``; a head with no valid
+    token in its attended pages gets zero rows.  Returns [Gq][d] per slot.
     """
     units = group_units(attended)
     U = len(units)
@@ -315,7 +320,8 @@ def decode_group_split(q_slots: Sequence[np.ndarray], K_slots: Sequence[np.ndarr
                 if toks:
                     parts.append(attention_lse(q_slots[j][g], K_slots[j][toks],
                                                V_slots[j][toks], scale))
-            rows.append(lse_combine(parts)[0])
+            rows.append(lse_combine(parts)[0] if parts else
+                        np.zeros(np.asarray(V_slots[j]).shape[1]))
         out.append(np.stack(rows))
     return out
 
@@ -323,8 +329,8 @@ def decode_group_split(q_slots: Sequence[np.ndarray], K_slots: Sequence[np.ndarr
 def decode_head(q_group: np.ndarray, K: np.ndarray, V: np.ndarray,
                 pages: Sequence[int], P: int, scale: float) -> np.ndarray:
     """Attention of a KV head's query group over the valid tokens of its
-    attended pages (the result split-K + combine reaches up to rounding).
-    Returns [Gq][d]."""
+    attended pages (the result split-K + combine reaches up to rounding);
+    zero rows when there is none.  Returns [Gq][d]."""
     n = K.shape[0]
     toks = [t for p in pages for t in page_token_ids(int(p), n, P)]
     return np.stack([attention(q_group[g], K[toks], V[toks], scale)

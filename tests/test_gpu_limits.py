@@ -1,10 +1,12 @@
-"""Parity at the library's size limits, through the C ABI.
+"""Parity at the library's size limits and on empty heads, through the C ABI.
 
 The top-K keeps a head's scores in LDS, which caps a head at 8192 pages
 (131072 tokens) and K at 1024; both limits are taken here, with heavy
 score ties and -inf (null) pages in the top-K case, and end to end on a
 request whose heads reach the page limit (so one head spans thousands of
-units and its query rows merge hundreds of split partials)."""
+units and its query rows merge hundreds of split partials).  At the other
+end, heads holding no token at all (a cache before its first prefill
+chunk)."""
 
 from __future__ import annotations
 
@@ -73,3 +75,30 @@ def test_longest_heads_end_to_end(topk):
     check_layer(step, 0, step.queries()[0], [0], st)
     assert st.minmax_checked == sum(-(-int(x) // P) for x in wl.n[0, 0])
     assert_output_bar(st, f"longest heads topk={topk} S={step.S[0].tolist()}")
+
+
+@pytest.mark.parametrize("topk", [None, 3])
+def test_heads_without_tokens(topk):
+    """Heads with n = 0, among them every head of one request's group and a
+    whole request: no page, an all -inf score row, an empty selection
+    (count 0, -1 padding), zero output rows; the other heads match the
+    oracle as usual."""
+    require_gpu()
+    wl = make_workload("llama8b_ragged", b=3, N=400, Hq=32, d=128, dtype="f16", Hp=2, topk=topk)
+    wl.n[0, 0, :] = [0, 40, 1, 0, 300, 17, 64, 0]
+    wl.n[1, 0, :] = [0, 0, 0, 0, 0, 0, 0, 0]
+    wl.n[2, 0, :] = [16, 0, 33, 250, 0, 5, 2, 129]
+    say(f"[case] heads without tokens topk={topk}")
+    step = DecodeStep(wl, device="cuda")
+    c = wl.cfg
+    st = Stats()
+    check_layer(step, 0, step.queries()[0], range(c.b), st)
+    assert_output_bar(st, f"heads without tokens topk={topk}")
+    out = step.bufs[0].out.cpu().numpy()
+    for r in range(c.b):
+        for h in range(c.Hkv):
+            if wl.n[r, 0, h] == 0:
+                assert np.all(out[r, h * c.Gq:(h + 1) * c.Gq] == 0.0), f"r={r} h={h}"
+    if topk:
+        cnt = step.bufs[0].sel_count.cpu().numpy()
+        assert np.array_equal(cnt == 0, wl.n[:, 0, :] == 0)

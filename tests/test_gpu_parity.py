@@ -147,20 +147,25 @@ def test_edge_cases(Hp, d, Hq, dtype, n_list, topk):
         assert_output_bar(st, f"edge T={T}")
 
 
+@pytest.mark.parametrize("whole_group", [False, True])
 @pytest.mark.parametrize("topk", [None, 2])
-def test_null_page_entries(topk):
+def test_null_page_entries(topk, whole_group):
     """Null (-1) page-table entries: the min-max builder leaves their blocks
     untouched, scoring gives them -inf, and decode leaves their tokens out.
-    Page 0 of every group stays valid, so every head keeps some tokens."""
+    Page 0 of every group stays valid, except that with whole_group every
+    page of request 1's group 1 is null: its heads attend nothing and their
+    query heads get zero rows."""
     require_gpu()
     wl = make_workload("llama8b_ragged", b=2, N=400, Hq=32, d=128, dtype="f16", Hp=4, topk=topk)
     wl.n[0, 0, :] = [40, 1, 16, 300, 64, 65, 17, 2]
     wl.n[1, 0, :] = [100, 33, 250, 49, 16, 80, 5, 129]
-    say(f"[case] null pages topk={topk}")
+    say(f"[case] null pages topk={topk} whole_group={whole_group}")
     c = wl.cfg
     step = DecodeStep(wl, device="cuda")
     cache, lay = step.caches[0], step.layouts[0]
     nulls = {(0, 0): [1], (0, 1): [2, 5], (1, 0): [3], (1, 1): [1, 7]}
+    if whole_group:
+        nulls[(1, 1)] = list(range(lay.page_table.shape[2]))
     pt = lay.page_table.copy()
     for (r, i), ps in nulls.items():
         pt[r, i, [p for p in ps if p < pt.shape[2]]] = -1
@@ -174,7 +179,7 @@ def test_null_page_entries(topk):
     mm = cache.minmax.double().cpu().numpy()
     q64 = q.double().cpu().numpy()
     buf = step.bufs[0]
-    hit = 0
+    hit = empty = 0
     for r in range(c.b):
         for h in range(c.Hkv):
             pos = int(step.head_slot[0, h])
@@ -211,7 +216,11 @@ def test_null_page_entries(topk):
             ref = O.decode_head(qg, K64, V64, pages, c.P, step.scale)
             err = float(np.abs(out[r, h * c.Gq:(h + 1) * c.Gq] - ref).max())
             assert err <= OUT_MAX_ABS, f"r={r} h={h} err={err}"
+            if len(pages) == 0:
+                assert np.all(out[r, h * c.Gq:(h + 1) * c.Gq] == 0.0)
+                empty += 1
     assert hit >= 4, "the case should null some pages of real heads"
+    assert empty == (c.Hp if whole_group else 0)
 
 
 def test_deterministic():

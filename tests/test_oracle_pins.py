@@ -346,6 +346,31 @@ def test_split_invariance():
         assert np.allclose(a, b, rtol=1e-12, atol=1e-14)
 
 
+def test_heads_without_tokens_give_zero_rows():
+    """A head holding no token, and a head whose attended list is empty,
+    attend nothing: zero rows (the empty softmax sum carries no weight), at
+    every split count, while the group's other heads keep their dense
+    result.  An all-empty merge is (0, -inf), like attention over no token."""
+    rng = np.random.default_rng(21)
+    P = 4
+    n_list = [0, 9, 6, 3]
+    q, K, V = _group_case(rng, n_list)
+    attended = [[], [0, 1, 2], [], [0]]
+    U = sum(len(a) for a in attended)
+    for S in (1, 2, U, U + 2):
+        got = O.decode_group_split(q, K, V, attended, P, S, 0.5)
+        assert np.array_equal(got[0], np.zeros((2, 8)))
+        assert np.array_equal(got[2], np.zeros((2, 8)))
+        for j in (1, 3):   # every token of these heads is attended
+            dense = np.array([_attention_naive(q[j][g], K[j], V[j], 0.5) for g in range(2)])
+            assert np.allclose(got[j], dense, rtol=1e-12, atol=1e-14)
+    assert np.array_equal(O.decode_head(q[0], K[0], V[0], [], P, 0.5), np.zeros((2, 8)))
+    o, lse = O.lse_combine([(np.ones(3), -math.inf), (np.full(3, 5.0), -math.inf)])
+    assert np.array_equal(o, np.zeros(3)) and lse == -math.inf
+    with pytest.raises(ValueError):
+        O.lse_combine([])
+
+
 def test_full_budget_topk_is_dense():
     """With K >= np, attention over the selected pages is dense attention
     over every retained token."""
