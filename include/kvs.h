@@ -130,7 +130,8 @@ typedef struct kvs_paged_kv {
  * selection).  Pages with a null table entry and block indices outside
  * [0, num_meta) are skipped.
  * Blocks of pages beyond a head's n are left untouched.
- * Runs once per page fill, not per decode step.
+ * Runs once per page fill, not per decode step.  Needs b*Hkv <= 16383
+ * (KVS_EUNSUPPORTED otherwise).
  */
 int kvs_build_minmax(const kvs_paged_kv* cache, void* stream);
 

@@ -105,6 +105,8 @@ extern "C" int kvs_build_minmax(const kvs_paged_kv* cache, void* stream) {
   clear_error();
   CacheView c;
   if (int rc = check_cache(cache, true, "kvs_build_minmax", &c)) return rc;
+  if ((int64_t)c.b * c.Hkv > kMaxScoreHeads)   // the heads' page counts are scanned in LDS
+    return set_error(KVS_EUNSUPPORTED, "kvs_build_minmax: b*Hkv > %d", kMaxScoreHeads);
   if (hipError_t e = launch_minmax(c, (hipStream_t)stream)) return hip_error(e, "kvs_build_minmax");
   return KVS_OK;
 }

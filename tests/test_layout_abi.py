@@ -148,6 +148,7 @@ class _FakeCache:
     (dict(b=0), kvs.KVS_EINVAL),
     (dict(meta_base=0), kvs.KVS_EINVAL),
     (dict(num_meta=0), kvs.KVS_EINVAL),
+    (dict(b=2048, Hkv=8, Hq=32), kvs.KVS_EUNSUPPORTED),   # b*Hkv above the LDS scan
 ])
 def test_validation_before_launch(kw, code):
     L = _lib()
