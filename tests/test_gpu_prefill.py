@@ -24,6 +24,7 @@ pytestmark = pytest.mark.gpu
     ("gemma3_mixed", dict(b=3, L=2, N=4096, topk=16), 512),
     ("llama8b_ragged", dict(b=2, N=700, Hp=2, dtype="bf16"), 100),
     ("longctx_skew", dict(b=1, L=2, N=600), 8),        # small budgets: chunks that keep nothing
+    ("llama8b_ragged", dict(b=1, N=20000), 8192),      # the longest chunk the call takes
 ])
 def test_prefill_parity(name, ov, C):
     require_gpu()
