@@ -187,11 +187,11 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     };
     auto load_k = [&](const uint16_t* kt, uint4 (&dst)[TL]) {
 #pragma unroll
-      for (int k = 0; k < TL; ++k) dst[k] = ld16(kt + v_off + RPL * k * D);
+      for (int k = 0; k < TL; ++k) dst[k] = ld16_once(kt + v_off + RPL * k * D);
     };
     auto load_v = [&](const uint16_t* kt, uint4 (&dst)[TL]) {
 #pragma unroll
-      for (int k = 0; k < TL; ++k) dst[k] = ld16(kt + P * D + v_off + RPL * k * D);
+      for (int k = 0; k < TL; ++k) dst[k] = ld16_once(kt + P * D + v_off + RPL * k * D);
     };
 #pragma unroll
     for (int b = 0; b < DEPTH; ++b) {

@@ -142,6 +142,15 @@ __device__ __forceinline__ float across_max(float v) {
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// 16-byte load of data that is read once per pass (K/V tiles, page bounds):
+// marked non-temporal, so the caches do not keep it at the expense of the
+// data that is reused (page tables, queries, partials).
+__device__ __forceinline__ uint4 ld16_once(const void* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 }  // namespace kvs

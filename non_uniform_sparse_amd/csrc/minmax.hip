@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kFlatThreads) void minmax_kernel(CacheView c) {
       };
       auto load = [&](const uint16_t* t, uint4 (&dst)[TL]) {
 #pragma unroll
-        for (int k = 0; k < TL; ++k) dst[k] = ld16(t + RPL * k * D);
+        for (int k = 0; k < TL; ++k) dst[k] = ld16_once(t + RPL * k * D);
       };
       auto reduce_store = [&](int i, const uint4 (&src)[TL]) {
         const int phys = __builtin_amdgcn_readlane(my_phys, i);

@@ -95,8 +95,8 @@ __global__ __launch_bounds__(64 * kPagesPerBlock) void place_kernel(
   for (int k = 0; k < TL; ++k) {   // row rg + RPL k of the page, clamped into the chunk's rows
     const int pos = min(max(p * P + rg + RPL * k, lo_pos), hi_pos - 1);
     const int64_t t = kept[pos - n];
-    kr[k] = ld16(ksrc + t * D);
-    vr[k] = ld16(vsrc + t * D);
+    kr[k] = ld16_once(ksrc + t * D);
+    vr[k] = ld16_once(vsrc + t * D);
   }
   float lo[8], hi[8];
 #pragma unroll

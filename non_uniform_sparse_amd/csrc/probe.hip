@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kFlatThreads) void probe_kernel(CacheView c, const 
     auto load = [&](int i, uint4 (&dst)[LOADS], bool& ok) {
       const uint16_t* t = tile(i, ok);
 #pragma unroll
-      for (int k = 0; k < LOADS; ++k) dst[k] = ld16(t + 512 * k);
+      for (int k = 0; k < LOADS; ++k) dst[k] = ld16_once(t + 512 * k);
     };
     auto fold = [&](const uint4 (&src)[LOADS], bool ok) {
       uint32_t x = 0;

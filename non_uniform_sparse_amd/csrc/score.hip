@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(CacheView c, const uint
         m = m < 0 ? 0 : (m > last ? last : m);
         const uint16_t* bp = mmb + m * (2 * D);
 #pragma unroll
-        for (int k = 0; k < LOADS; ++k) dst[u][k] = ld16(bp + 64 * k);
+        for (int k = 0; k < LOADS; ++k) dst[u][k] = ld16_once(bp + 64 * k);
         pt[u] = ptrow[p];
       }
     };
