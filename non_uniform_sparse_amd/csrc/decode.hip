@@ -18,7 +18,8 @@
 // lane l takes channels 8*(l % COLS) .. +8 of rows rg + RPL*k, rg = l / COLS,
 // k < TL, with COLS = d/8, RPL = 64/COLS, TL = 16/RPL.  Every load
 // instruction reads RPL whole rows (1 KB), so the 4 KB (d=128) or 8 KB
-// (d=256) K and V tiles stream in fully coalesced 16-byte accesses.  Logits
+// (d=256) K and V tiles stream in fully coalesced 16-byte accesses, marked
+// non-temporal (each tile is read once per step).  Logits
 // are pair-dots of q with K summed over the row's COLS lanes; p*V is
 // accumulated per lane and reduced over the row groups once per head.
 #include <algorithm>
@@ -179,7 +180,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
       my_j = j;
     }
     // Tile of unit t; a missing page reads page 0 instead (always valid
-    // memory; such units are skipped), so every load is unconditional.
+    // memory; such units are skipped), so no load depends on a lane's data.
     auto tile = [&](int t) {
       const int phys = __builtin_amdgcn_readlane(my_phys, t);
       const int j = __builtin_amdgcn_readlane(my_j, t);
@@ -209,12 +210,16 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
         begin_head(j);
         cur_j = j;
       }
-      // tile to prefetch (past the batch end, the last unit re-reads its own:
-      // harmless, cached)
-      const uint16_t* nt = tile(t + DEPTH < nb ? t + DEPTH : nb - 1);
+      // tile to prefetch; past the batch end there is none (the condition is
+      // uniform over the wave, and the tiles are read with non-temporal
+      // loads, so re-reading the last one would go back to HBM)
+      const bool more = t + DEPTH < nb;
+      const uint16_t* nt = tile(more ? t + DEPTH : nb - 1);
       if (phys < 0 || valid <= 0) {
-        load_k(nt, kc[B]);
-        load_v(nt, vr[B]);
+        if (more) {
+          load_k(nt, kc[B]);
+          load_v(nt, vr[B]);
+        }
         return;
       }
       // K rows -> LDS, then back in MFMA operand layout (the global loads stay
@@ -222,7 +227,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
       for (int k = 0; k < TL; ++k)
         *reinterpret_cast<uint4*>(ktile + w_lds + RPL * k * KROW) = kc[B][k];
-      load_k(nt, kc[B]);   // K registers free: fetch a later unit's K
+      if (more) load_k(nt, kc[B]);   // K registers free: fetch a later unit's K
       // The workgroup is one wave and a wave's LDS operations execute in
       // order; the compiler barrier keeps the reads after the writes and the
       // LDS-only wait (vmcnt, expcnt left at their maxima) leaves the
@@ -287,7 +292,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
           }
         }
       }
-      load_v(nt, vr[B]);   // V consumed: fetch a later unit's V
+      if (more) load_v(nt, vr[B]);   // V consumed: fetch a later unit's V
     };
     for (int t0 = 0; t0 < nb; t0 += DEPTH) {
       [&]<int... B>(std::integer_sequence<int, B...>) {

@@ -19,9 +19,9 @@
 // channel-interleaved, (min, max) per channel, so that one page of one head
 // is a single contiguous 4*d-byte block, and goes to block meta_base[r][h] +
 // p of the min-max cache, not to the page's physical KV slot: each head's
-// bounds form one contiguous run in page order.  Loads are unconditional (a
-// missing page reads page 0 and is discarded; indices are clamped into the
-// segment), which keeps the compiler's wait counting exact.
+// bounds form one contiguous run in page order.  K tiles are read with
+// non-temporal loads (each once per build), never past a batch's last page;
+// a missing page reads page 0 and is discarded.
 #include "flat_pages.h"
 #include "kvs_launch.h"
 
@@ -161,10 +161,10 @@ __global__ __launch_bounds__(kFlatThreads) void minmax_kernel(CacheView c) {
       };
       uint4 buf0[TL], buf1[TL];
       load(tile(0), buf0);
-      for (int i = 0; i < nb; i += 2) {
-        load(tile(min(i + 1, nb - 1)), buf1);
+      for (int i = 0; i < nb; i += 2) {   // no load past the batch (uniform tests)
+        if (i + 1 < nb) load(tile(i + 1), buf1);
         reduce_store(i, buf0);
-        load(tile(min(i + 2, nb - 1)), buf0);
+        if (i + 2 < nb) load(tile(i + 2), buf0);
         if (i + 1 < nb) reduce_store(i + 1, buf1);
       }
     }

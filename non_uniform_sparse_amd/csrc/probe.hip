@@ -8,9 +8,9 @@
 // The grid is resident-sized and each wave takes an even share of all heads'
 // units (flat_pages.h).  A unit's K tile and V tile are 2 P d contiguous
 // elements; 64 lanes read 16 bytes each per load instruction, and the next
-// unit's loads are issued before the current one is folded.  A missing
-// (null) page loads page 0's tile, which keeps the loads unconditional, and
-// those words are not folded.
+// unit's loads are issued before the current one is folded; no load reaches
+// past a segment's last unit.  A missing (null) page loads page 0's tile,
+// and those words are not folded.
 #include "flat_pages.h"
 #include "kvs_launch.h"
 
@@ -74,10 +74,10 @@ __global__ __launch_bounds__(kFlatThreads) void probe_kernel(CacheView c, const 
       acc ^= ok ? x : 0u;
     };
     load(i0, buf0, ok0);
-    for (int i = i0; i < i1; i += 2) {
-      load(min(i + 1, i1 - 1), buf1, ok1);
+    for (int i = i0; i < i1; i += 2) {   // no load past the segment (uniform tests)
+      if (i + 1 < i1) load(i + 1, buf1, ok1);
       fold(buf0, ok0);
-      load(min(i + 2, i1 - 1), buf0, ok0);
+      if (i + 2 < i1) load(i + 2, buf0, ok0);
       if (i + 1 < i1) fold(buf1, ok1);
     }
     t0 = seg_end;

@@ -19,9 +19,11 @@
 // l / 8, so each load instruction reads one whole 128-byte line of each of 8
 // neighbouring pages, and a page's sum is 3 DPP levels over its 8 lanes.
 // Rounds are double-buffered: the next round's loads are in flight while
-// the current one is scored.  Every load is unconditional (round indices and
-// pages are clamped into the segment, repeats hit the cache), which keeps
-// the compiler's wait counting exact.  The page table is read beside the
+// the current one is scored; no round past the segment's last is loaded
+// (the test is uniform over the wave).  Inside a round the loads are
+// unconditional: lanes past the segment's end read its last page again,
+// within the same instructions.  The bounds are read with non-temporal loads
+// (each is read once per pass).  The page table is read beside the
 // bounds only to give null pages -inf; pages past a head's end get -inf
 // from a final block-strided fill.  The butterfly order is fixed:
 // deterministic.
@@ -134,10 +136,10 @@ __global__ __launch_bounds__(kThreads) void score_kernel(CacheView c, const uint
     };
     const int rounds = (p1 - p0 + RP - 1) / RP;
     issue(0, mmv[0], ptv[0]);
-    for (int rd = 0; rd < rounds; rd += 2) {
-      issue(min(rd + 1, rounds - 1), mmv[1], ptv[1]);
+    for (int rd = 0; rd < rounds; rd += 2) {   // no round past the segment's last
+      if (rd + 1 < rounds) issue(rd + 1, mmv[1], ptv[1]);
       score(rd, mmv[0], ptv[0]);
-      issue(min(rd + 2, rounds - 1), mmv[0], ptv[0]);
+      if (rd + 2 < rounds) issue(rd + 2, mmv[0], ptv[0]);
       if (rd + 1 < rounds) score(rd + 1, mmv[1], ptv[1]);
     }
 
