@@ -187,6 +187,55 @@ def rerank_reuse_report(configs, period: int = 16, unstable_frac: float = 0.25,
     return out
 
 
+def sparse_dense_report(configs, reps: int = 20) -> dict:
+    """Top-K sparse decode against dense decode on the same caches (FlexiCache
+    summary, Experiments: the decode microbenchmark compares the two).  The
+    sparse step is score + top-K + decode over the selected pages; the dense
+    step decodes every retained page with its own split plan (no top-K cap
+    on the budgets).  Both are captured as graphs (request micro-batches as
+    the headline uses them) and replayed; small working sets are preceded by
+    a 1 GiB read, as in the headline protocol."""
+    out = {}
+    for name in configs:
+        ov = {"L": 8} if name == "gemma3_mixed" else {}
+        res, kv_bytes = {}, {}
+        for mode in ("sparse", "dense"):
+            wl = make_workload(name, **ov) if mode == "sparse" else \
+                make_workload(name, topk=None, **ov)
+            c = wl.cfg
+            step = DecodeStep(wl, device="cuda", poison=False,
+                              microbatches=default_microbatches(wl))
+            qs = step.queries()
+            g = step.capture(qs)               # runs the step once eagerly first
+            torch.cuda.synchronize()
+            kv_bytes[mode] = sum(algorithmic_bytes(step, l)["kv"] for l in range(c.L))
+            flush = torch.ones(1 << 27, dtype=torch.int64, device="cuda") \
+                if kv_bytes[mode] < 8e9 else None
+            times = []
+            for _ in range(reps + 2):
+                if flush is not None:
+                    flush.sum()
+                a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                g.replay()
+                b_.record()
+                b_.synchronize()
+                times.append(a.elapsed_time(b_) * 1e3)
+            res[mode] = statistics.median(times[2:])
+            del g, step, flush
+            torch.cuda.empty_cache()
+        out[name] = {
+            "layers": c.L, "requests": c.b, "topk_pages": CONFIGS[name].topk,
+            "us_per_step_sparse": round(res["sparse"], 1),
+            "us_per_step_dense": round(res["dense"], 1),
+            "speedup": round(res["dense"] / res["sparse"], 3),
+            "kv_bytes_sparse": int(kv_bytes["sparse"]), "kv_bytes_dense": int(kv_bytes["dense"]),
+            "dense_kv_GBps": round(kv_bytes["dense"] / (res["dense"] * 1e-6) / 1e9, 1),
+            "includes": "sparse: scoring + top-K + decode; dense: decode of every retained page",
+        }
+    return out
+
+
 def prefill_report(configs, chunk: int = 2048) -> dict:
     """Chunked prefill under Budget Reservation (Tangram review, 3.1): every
     chunk of every layer, selection + compaction + page bounds in one
@@ -512,6 +561,10 @@ def main() -> int:
     ap.add_argument("--codec", nargs="?", const="llama7b_chunk", default=None, metavar="CHUNK",
                     help="encode a KV chunk on the host and time its GPU decode, print it "
                          "and exit")
+    ap.add_argument("--sparse-vs-dense", nargs="*", default=None, metavar="CONFIG",
+                    help="time the top-K sparse step against dense decode on the same caches "
+                         "(default configs: flexicache_topk, gemma3_mixed at 8 layers), print "
+                         "that record and exit")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--skew", nargs="*", default=None, metavar="CONFIG",
                     help="measure per-workgroup duration skew (planned vs uniform split "
@@ -537,6 +590,10 @@ def main() -> int:
         return 0
     if args.codec is not None:
         print(json.dumps({"codec": codec_report(args.codec)}))
+        return 0
+    if args.sparse_vs_dense is not None:
+        print(json.dumps({"sparse_vs_dense": sparse_dense_report(
+            args.sparse_vs_dense or ["flexicache_topk", "gemma3_mixed"])}))
         return 0
     if args.tier is not None:
         print(json.dumps({"tier": tier_report(args.tier)}))
