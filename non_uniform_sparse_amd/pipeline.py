@@ -30,10 +30,12 @@ from .workloads import Workload, torch_dtype
 __all__ = ["DecodeStep", "splits_per_request", "topk_cap", "default_microbatches"]
 
 
-def splits_per_request(W: int, b: int, G: int, mean_units: float, min_units: int = 8) -> int:
+def splits_per_request(W: int, b: int, G: int, mean_units: float, min_units: int = 4) -> int:
     """Splits T of one request's layer: enough workgroups to fill the chip
     (W concurrent, shared by b requests), but no split smaller than about
-    ``min_units`` pages and never fewer than one split per group."""
+    ``min_units`` pages and never fewer than one split per group.  The floor
+    only binds for small batches of short requests (measured on a one-request
+    step: 4 pages per split 12% faster than 8; 2 no faster than 4)."""
     t = W // max(1, b)
     t = min(t, max(1, math.ceil(mean_units / min_units)))
     return max(G, t)
