@@ -198,7 +198,7 @@ __global__ __launch_bounds__(kMaxThreads) void codec_decode_kernel(CodecArgs a) 
         for (int k = steps - 1; k >= 0; --k) {
           const int m = x + (1 << k);
           const uint32_t c = s_cdf[lo_off + min(m, last)];
-          x = (m <= last) & (c <= v) ? m : x;
+          x = ((m <= last) & (c <= v)) ? m : x;
         }
         const uint32_t c_lo = s_cdf[lo_off + x];
         const uint32_t c_hi = x < last ? s_cdf[lo_off + x + 1] : 65536u;
