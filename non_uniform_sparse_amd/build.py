@@ -18,7 +18,7 @@ LIB_STAMPS = os.path.join(PKG, "libkvs_stamps.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function"]
+COMMON = ["-O3", "-fPIC", "-std=c++20", "-Wall", "-Wno-unused-function"]
 # gfx950 device code; packed-fp32 instructions are switched off.
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-munsafe-fp-atomics"]

@@ -357,7 +357,6 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
       const float wt = __builtin_amdgcn_exp2f(lw - M);   // 0 for an empty split
       den += wt;
       const int nsp = min(64, w_hi - w0 + 1);
-#pragma unroll 2
       for (int s8 = 0; s8 < nsp; s8 += 8) {
         const int sp = s8 + sl;
         const float w = __shfl(wt, sp, 64);
