@@ -60,7 +60,8 @@ class DecodeLoop:
                        else np.array(stable, dtype=bool))       # [L][Hkv]
         self.n0 = [cache.seq_len.clone() for cache in self.ds.caches]
         # every step's inputs, resident on the device before any step runs
-        self.q = [[wl.step_q(t, l, device) for l in range(c.L)] for t in range(steps)]
+        qs = [wl.step_qs(steps, l, device) for l in range(c.L)]
+        self.q = [[qs[l][t] for l in range(c.L)] for t in range(steps)]
         self.kv = [[wl.step_kv(t, l, device) for l in range(c.L)] for t in range(steps)]
 
     def heads_due(self, t: int, l: int) -> np.ndarray:

@@ -170,7 +170,8 @@ class TieredLoop:
         self.n0 = [cc.seq_len.clone() for cc in self.ds.caches]
         self.moved = [torch.zeros((c.b, c.Hkv), dtype=torch.int32, device=device)
                       for _ in range(c.L)]
-        self.q = [[wl.step_q(t, l, device) for l in range(c.L)] for t in range(steps)]
+        qs = [wl.step_qs(steps, l, device) for l in range(c.L)]
+        self.q = [[qs[l][t] for l in range(c.L)] for t in range(steps)]
         self.kv = ([[wl.step_kv(t, l, device) for l in range(c.L)] for t in range(steps)]
                    if append else None)
 

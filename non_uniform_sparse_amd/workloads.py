@@ -31,13 +31,18 @@ drawn by a torch generator seeded from (seed, r, lam, pos).  Head h of layer
 l of request r stored at pool position pos reads the first n[r,l,h] tokens
 of bank (r, l mod data_layers, pos).  The tiny workload instead draws a full
 4096-token stream per head and keeps the chosen positions.
+
+Decoding over steps.  The token appended at step t is N(0,1).  The query
+drifts from step to step: an AR(1) process with per-step correlation
+QUERY_RHO (``step_qs``), so that top-K sets turn over between reranks at
+the rate the pages report.
 """
 
 from __future__ import annotations
 
 import math
 from dataclasses import dataclass, field, replace
-from typing import Dict, Optional, Tuple
+from typing import Dict, List, Optional, Tuple
 
 import numpy as np
 import torch
@@ -96,6 +101,10 @@ CONFIGS: Dict[str, Config] = {
 
 def torch_dtype(name: str) -> torch.dtype:
     return {"f16": torch.float16, "bf16": torch.bfloat16}[name]
+
+
+# Step-to-step correlation of decode queries (see Workload.step_qs).
+QUERY_RHO = 0.997
 
 
 def _mix(*vals: int) -> int:
@@ -188,12 +197,30 @@ class Workload:
         return K, V
 
     # ---------------------------------------------------------- decode steps --
-    def step_q(self, t: int, l: int, device="cpu") -> torch.Tensor:
-        """Queries of decode step t of layer l: [b][Hq][d] ~ N(0,1)."""
+    def step_qs(self, steps: int, l: int, device="cpu") -> List[torch.Tensor]:
+        """Queries of decode steps 0 .. steps-1 of layer l, each [b][Hq][d].
+
+        A query drifts from step to step rather than being drawn afresh: an
+        AR(1) process q_t = rho q_{t-1} + sqrt(1 - rho^2) e_t with q_0 = e_0
+        and e_t ~ N(0,1) (every q_t is N(0,1) too).  rho = QUERY_RHO is set
+        so that the top-K set of a flexicache_topk head re-selected every 16
+        steps changes by about 30% (simulated: 31%), inside the 23-35% of
+        promoted pages per rerank that the FlexiCache summary (tiered
+        placement) reports for real attention.  Computed in fp32, then cast
+        to the workload dtype."""
         c = self.cfg
-        g = torch.Generator(device=device).manual_seed(_mix(c.seed, 4, t, l))
-        x = torch.randn((c.b, c.Hq, c.d), generator=g, device=device, dtype=torch.float32)
-        return x.to(torch_dtype(c.dtype))
+        out, q = [], None
+        a = math.sqrt(1.0 - QUERY_RHO * QUERY_RHO)
+        for t in range(steps):
+            g = torch.Generator(device=device).manual_seed(_mix(c.seed, 4, t, l))
+            e = torch.randn((c.b, c.Hq, c.d), generator=g, device=device, dtype=torch.float32)
+            q = e if q is None else QUERY_RHO * q + a * e
+            out.append(q.to(torch_dtype(c.dtype)))
+        return out
+
+    def step_q(self, t: int, l: int, device="cpu") -> torch.Tensor:
+        """Queries of decode step t of layer l (see ``step_qs``)."""
+        return self.step_qs(t + 1, l, device)[t]
 
     def step_kv(self, t: int, l: int, device="cpu") -> Tuple[torch.Tensor, torch.Tensor]:
         """Key and value of the token decoded at step t, for every (request,
