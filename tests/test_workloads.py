@@ -56,3 +56,28 @@ def test_offsets_shift_keys():
     assert torch.allclose(diff[:, chans], torch.full((16, 8), 3.0), atol=2e-2)
     other = [c for c in range(wl.cfg.d) if c not in chans]
     assert torch.all(diff[:, other] == 0)
+
+
+def test_step_queries_drift_as_ar1():
+    """Decode-step queries: q_0 is a fresh N(0,1) draw and every later q_t is
+    rho q_{t-1} plus sqrt(1 - rho^2) of that step's fresh draw, so each q_t
+    stays N(0,1) and consecutive queries correlate by rho; step_q(t) is the
+    t-th element of the sequence."""
+    from non_uniform_sparse_amd import workloads as W
+    wl = make_workload("flexicache_topk", b=8, dtype="bf16")
+    c = wl.cfg
+    qs = wl.step_qs(12, 0)
+    assert len(qs) == 12 and qs[0].shape == (c.b, c.Hq, c.d)
+    assert torch.equal(wl.step_q(7, 0), qs[7])
+    rho = W.QUERY_RHO
+    # the recursion, in fp32 from the same fresh draws
+    e = [torch.randn((c.b, c.Hq, c.d), generator=torch.Generator().manual_seed(
+        W._mix(c.seed, 4, t, 0)), dtype=torch.float32) for t in range(12)]
+    q = e[0]
+    for t in range(1, 12):
+        q = rho * q + (1 - rho * rho) ** 0.5 * e[t]
+    assert torch.equal(qs[11], q.to(qs[11].dtype))
+    # statistics over 8 x 32 x 128 values
+    a, b = qs[10].float(), qs[11].float()
+    assert abs(float(b.std()) - 1.0) < 0.02
+    assert abs(float((a * b).mean()) / float((a * a).mean()) - rho) < 0.01
