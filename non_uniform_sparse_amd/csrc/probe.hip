@@ -6,11 +6,13 @@
 // chip; the decode's own rate is set against it.
 //
 // The grid is resident-sized and each wave takes an even share of all heads'
-// units (flat_pages.h).  A unit's K tile and V tile are 2 P d contiguous
-// elements; 64 lanes read 16 bytes each per load instruction, and the next
-// unit's loads are issued before the current one is folded; no load reaches
-// past a segment's last unit.  A missing (null) page loads page 0's tile,
-// and those words are not folded.
+// units (flat_pages.h).  As in the decode, a wave resolves the physical ids
+// of 64 units at a time, lane-parallel (selection entry, then page table),
+// and reads them back with readlane.  A unit's K tile and V tile are 2 P d
+// contiguous elements; 64 lanes read 16 bytes each per load instruction
+// (non-temporal), and the next unit's loads are issued before the current
+// one is folded; no load reaches past a batch's last unit.  A missing (null)
+// page loads page 0's tile, and those words are not folded.
 #include "flat_pages.h"
 #include "kvs_launch.h"
 
@@ -52,18 +54,8 @@ __global__ __launch_bounds__(kFlatThreads) void probe_kernel(CacheView c, const 
     const int gi = head_ok ? hs / c.Hp : 0, slot = head_ok ? hs % c.Hp : 0;
     const int32_t* ptrow = c.page_table + ((int64_t)r * c.G + gi) * c.maxpg;
     const int32_t* srow = sel ? sel + (int64_t)rh * K : nullptr;
-    // unit i's tile; ok = false for a null or out-of-range page
-    auto tile = [&](int i, bool& ok) {
-      int p = srow ? srow[i] : i;
-      p = clampi(p, 0, c.maxpg - 1);
-      const int phys = ptrow[p];
-      ok = head_ok && phys >= 0 && phys < c.num_pages;
-      return kvb + (ok ? ((int64_t)phys * c.Hp + slot) * 2 * P * D : 0);
-    };
     uint4 buf0[LOADS], buf1[LOADS];
-    bool ok0, ok1;
-    auto load = [&](int i, uint4 (&dst)[LOADS], bool& ok) {
-      const uint16_t* t = tile(i, ok);
+    auto load = [&](const uint16_t* t, uint4 (&dst)[LOADS]) {
 #pragma unroll
       for (int k = 0; k < LOADS; ++k) dst[k] = ld16_once(t + 512 * k);
     };
@@ -73,12 +65,29 @@ __global__ __launch_bounds__(kFlatThreads) void probe_kernel(CacheView c, const 
       for (int k = 0; k < LOADS; ++k) x ^= src[k].x ^ src[k].y ^ src[k].z ^ src[k].w;
       acc ^= ok ? x : 0u;
     };
-    load(i0, buf0, ok0);
-    for (int i = i0; i < i1; i += 2) {   // no load past the segment (uniform tests)
-      if (i + 1 < i1) load(i + 1, buf1, ok1);
-      fold(buf0, ok0);
-      if (i + 2 < i1) load(i + 2, buf0, ok0);
-      if (i + 1 < i1) fold(buf1, ok1);
+    for (int b0 = i0; b0 < i1; b0 += 64) {
+      const int nb = min(64, i1 - b0);
+      // lane u resolves unit b0 + u (selection entry, then page table), as
+      // the decode does; -1: null or out-of-range page
+      int my_phys = -1;
+      if (lane < nb) {
+        int p = srow ? srow[b0 + lane] : b0 + lane;
+        p = clampi(p, 0, c.maxpg - 1);
+        const int ph = ptrow[p];
+        if (head_ok && ph >= 0 && ph < c.num_pages) my_phys = ph;
+      }
+      auto phys_of = [&](int u) { return __builtin_amdgcn_readlane(my_phys, u); };
+      auto tile = [&](int u) {
+        const int ph = phys_of(u);
+        return kvb + (ph >= 0 ? ((int64_t)ph * c.Hp + slot) * 2 * P * D : 0);
+      };
+      load(tile(0), buf0);
+      for (int u = 0; u < nb; u += 2) {   // no load past the batch (uniform tests)
+        if (u + 1 < nb) load(tile(u + 1), buf1);
+        fold(buf0, phys_of(u) >= 0);
+        if (u + 2 < nb) load(tile(u + 2), buf0);
+        if (u + 1 < nb) fold(buf1, phys_of(u + 1) >= 0);
+      }
     }
     t0 = seg_end;
     while (hh < BH && uni(pre[hh + 1]) <= t0) ++hh;
