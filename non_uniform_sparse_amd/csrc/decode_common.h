@@ -1,5 +1,5 @@
-// Pieces shared by the split-K decode kernel and its read-only twin: the
-// unit bookkeeping of one (request, group) and the lane geometry of a page.
+// Pieces of the split-K decode kernel: the unit bookkeeping of one
+// (request, group) and the lane geometry and math of a page.
 #pragma once
 
 #include <utility>
@@ -18,26 +18,27 @@ struct GroupUnits {
   int total;
 };
 
-// Heads and unit counts of group gi of request r, identical in both kernels.
+// Heads and unit counts of group gi of request r.  Lane h reads head h's
+// slot, length and selection count at once (no load waits on another), and
+// the heads of group gi fill their slots' entries.
 __device__ void group_units(const DecodeArgs& a, int r, int gi, GroupUnits* gu) {
   const CacheView& c = a.c;
   const int lane = threadIdx.x;
-  if (lane < kMaxHp) gu->head[lane] = -1;
+  if (lane < kMaxHp) {
+    gu->head[lane] = -1;
+    gu->count[lane] = 0;
+  }
   __syncthreads();
   for (int h = lane; h < c.Hkv; h += 64) {
     const int hs = c.head_slot[h];
-    if (hs >= 0 && hs < c.Hkv && hs / c.Hp == gi) gu->head[hs % c.Hp] = h;
-  }
-  __syncthreads();
-  if (lane < c.Hp) {
-    const int h = gu->head[lane];
-    int cnt = 0;
-    if (h >= 0) {
-      const int n = clampi(c.seq_len[r * c.Hkv + h], 0, P * c.maxpg);
-      cnt = (n + P - 1) / P;
-      if (a.sel) cnt = min(cnt, clampi(a.sel_count[r * c.Hkv + h], 0, a.K));
+    const int n = clampi(c.seq_len[r * c.Hkv + h], 0, P * c.maxpg);
+    const int sc = a.sel ? a.sel_count[r * c.Hkv + h] : 0;
+    if (hs >= 0 && hs < c.Hkv && hs / c.Hp == gi) {
+      int cnt = (n + P - 1) / P;
+      if (a.sel) cnt = min(cnt, clampi(sc, 0, a.K));
+      gu->head[hs % c.Hp] = h;
+      gu->count[hs % c.Hp] = cnt;
     }
-    gu->count[lane] = cnt;
   }
   __syncthreads();
   if (lane == 0) {
