@@ -547,6 +547,9 @@ def main() -> int:
     ap.add_argument("--microbatches", type=int, default=0,
                     help="request micro-batches, each on a stream of its own in the step graph "
                          "(0: one below 4 layers, else min(3, requests))")
+    ap.add_argument("--fused-select", choices=["auto", "on", "off"], default="auto",
+                    help="score + top-K in one launch per layer: auto (layers whose heads are of "
+                         "similar length), on, off")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill", nargs="*", default=None, metavar="CONFIG",
                     help="time the chunked prefill under Budget Reservation (default configs: "
@@ -622,7 +625,8 @@ def main() -> int:
     wl = make_workload(args.config)
     c = wl.cfg
     step = DecodeStep(wl, device=dev,
-                      microbatches=args.microbatches or default_microbatches(wl))
+                      microbatches=args.microbatches or default_microbatches(wl),
+                      fused={"auto": None, "on": True, "off": False}[args.fused_select])
     qs = step.queries()
     torch.cuda.synchronize()
     log(f"[bench] {c.name}: set-up {time.time() - t0:.1f} s, W={step.W}, T={step.T}, "
@@ -648,7 +652,7 @@ def main() -> int:
     # spin long enough for the host to enqueue the whole step, so the
     # kernels run back to back and the events time kernels, not host
     # launch latency.
-    kern = {"score": [], "topk": [], "decode_attn": []}
+    kern = {"score": [], "topk": [], "select": [], "decode_attn": []}
     for _ in range(args.steps):
         with torch.cuda.stream(stream):
             torch.cuda._sleep(int(cycles_per_ms * (2.0 + 0.4 * c.L)))
@@ -657,7 +661,14 @@ def main() -> int:
         marks = []
         for l in range(c.L):
             q = qs[l]
-            if c.topk:
+            if c.topk and step.fused[l]:
+                a, b_ = ev(), ev()
+                a.record(stream)
+                kvs.kvs_select_pages(step.caches[l], q, step.bufs[l].scores, c.topk,
+                                     step.bufs[l].sel, step.bufs[l].sel_count, stream)
+                b_.record(stream)
+                marks.append(("select", a, b_))
+            elif c.topk:
                 a, b_, d_ = ev(), ev(), ev()
                 a.record(stream)
                 kvs.kvs_score_pages(step.caches[l], q, step.bufs[l].scores, stream)
@@ -752,9 +763,13 @@ def main() -> int:
                 "frac": round(gbps / HBM_PEAK_GBPS, 4)}
     rows = {"a1_minmax_build": dict(row(mm_ms, "minmax_launch"),
                                     note="once per page fill, not part of the step")}
-    if c.topk:
+    if kern["score"]:
         rows["a2_score"] = row(kern["score"], "score_launch")
         rows["a3_topk"] = dict(row(kern["topk"], "topk_launch"), bound="latency")
+    if kern["select"]:
+        rows["a2_a3_select"] = dict(row(kern["select"], "score_launch"),
+                                    note="scores and top-K in one launch (kvs_select_pages); "
+                                         "bytes are the scoring's")
     rows["a4_plan"] = {"us_host": round(plan_us, 1), "note": f"S[{c.L}][{c.G}], host, ahead of time"}
     rows["a5_a6_decode_combine"] = row(kern["decode_attn"], "decode_launch")
     rows["gather_probe"] = {"us": round(pr_ms * 1e3, 2), "bytes": int(pr_bytes),
@@ -791,6 +806,7 @@ def main() -> int:
             "cache_flush_between_steps": flush is not None,
             "step_launch": "hip_graph",
             "microbatches": len(step.parts),
+            "fused_select_layers": int(sum(step.fused)),
         },
         "kernels_ms_avg": {k: round(statistics.mean(v), 5) for k, v in kern.items() if v},
         "rows": rows,

@@ -187,6 +187,24 @@ int kvs_topk_pages_heads(const float* scores, const int32_t* seq_len, int32_t P,
                          int32_t* sel, int32_t* sel_count, void* stream);
 
 /*
+ * kvs_score_pages followed by kvs_topk_pages with K, in one launch [F Core
+ * method]: the same scores, bit for bit, and the same selection.  One
+ * workgroup per (request, KV head) scores the head's pages into on-chip
+ * memory and selects from there, so a head's scores are never re-read and
+ * the selection needs no launch of its own; it pays off when the b*Hkv heads
+ * are many and of similar length (a long head holds its workgroup while the
+ * others idle).
+ *   q          as kvs_score_pages.
+ *   scores     device, [b][Hkv][max_group_pages] fp32 written as
+ *              kvs_score_pages writes it, or NULL: the scores are not stored.
+ *   K          1 <= K <= 1024.  max_group_pages <= 8192.
+ *   sel, sel_count  as kvs_topk_pages.
+ * Errors: as the two calls it replaces; nothing is launched on an error.
+ */
+int kvs_select_pages(const kvs_paged_kv* cache, const void* q, float* scores, int32_t K,
+                     int32_t* sel, int32_t* sel_count, void* stream);
+
+/*
  * Append the decoded token of every head to its ragged page [F Method: the
  * token being decoded joins the cache; T 3.2 Ragged Paging] and update that
  * page's min-max bounds in place [F Key observations, assumption 2].  For

@@ -196,6 +196,24 @@ extern "C" int kvs_topk_pages_heads(const float* scores, const int32_t* seq_len,
   return topk_impl(scores, seq_len, P, b, Hkv, max_pages, K, m, sel, sel_count, stream, fn);
 }
 
+extern "C" int kvs_select_pages(const kvs_paged_kv* cache, const void* q, float* scores,
+                                int32_t K, int32_t* sel, int32_t* sel_count, void* stream) {
+  clear_error();
+  static const char* fn = "kvs_select_pages";
+  CacheView c;
+  if (int rc = check_cache(cache, true, fn, &c)) return rc;
+  if (!q || !sel || !sel_count) return set_error(KVS_EINVAL, "%s: null q, sel or sel_count", fn);
+  if (!aligned16(q)) return set_error(KVS_EINVAL, "%s: q must be 16-byte aligned", fn);
+  if (K < 1 || K > kMaxK) return set_error(KVS_EINVAL, "%s: K=%d not in [1, %d]", fn, K, kMaxK);
+  if (c.maxpg > kMaxTopkPages)
+    return set_error(KVS_EUNSUPPORTED, "%s: max_group_pages=%d > %d", fn, c.maxpg, kMaxTopkPages);
+  if ((int64_t)c.b * c.Hkv * c.maxpg > 0x7fffffff)
+    return set_error(KVS_EUNSUPPORTED, "%s: b*Hkv*max_group_pages >= 2^31", fn);
+  if (hipError_t e = launch_select(c, q, scores, K, sel, sel_count, (hipStream_t)stream))
+    return hip_error(e, fn);
+  return KVS_OK;
+}
+
 extern "C" size_t kvs_prefill_workspace_bytes(int32_t b, int32_t Hkv, int32_t C) {
   if (b < 1 || Hkv < 1 || C < 1 || C > kMaxChunk) return 0;
   return prefill_workspace_bytes(b, Hkv, C);

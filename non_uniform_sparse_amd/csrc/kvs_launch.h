@@ -28,6 +28,8 @@ hipError_t launch_score(const CacheView& c, const void* q, float* scores, const 
 hipError_t launch_topk(const float* scores, const int32_t* seq_len, int P, int b, int Hkv,
                        int max_pages, int K, const HeadMask& heads, int32_t* sel,
                        int32_t* sel_count, hipStream_t s);
+hipError_t launch_select(const CacheView& c, const void* q, float* scores, int K, int32_t* sel,
+                         int32_t* sel_count, hipStream_t s);
 hipError_t launch_append(const CacheView& c, const HostTierView* tier, const void* k_new,
                          const void* v_new, hipStream_t s);
 hipError_t launch_prefill(const CacheView& c, const void* k_chunk, const void* v_chunk,

@@ -1,11 +1,9 @@
 // Quest-style page scores (FlexiCache summary, Core method): for a KV head h
 // and page p, max over the query heads g of h of
-//     sum_c max(q[g][c]*kmin[p][c], q[g][c]*kmax[p][c]).
-// Since kmin <= kmax, the larger product is q*kmax when q >= 0 and q*kmin
-// when q < 0.  The metadata holds (min, max) per channel side by side, so
-// for each channel pair one v_perm_b32 whose byte selector comes from q's
-// sign bits picks the right bound of both channels, and one pair-dot adds
-// the two products (equal values, one fewer product).
+//     sum_c max(q[g][c]*kmin[p][c], q[g][c]*kmax[p][c]),
+// computed per page as quest_bound.h describes (one v_perm_b32 picks the
+// bound each channel's sign needs, one pair-dot adds two channels, a fixed
+// DPP butterfly sums a page's 8 lanes: deterministic).
 //
 // The work is a stream: every head's bounds are one contiguous run of
 // 4*d-byte blocks (block meta_base[r][h] + p), and the read is bound by HBM.
@@ -14,35 +12,17 @@
 // the prefix sum of the heads' page counts in LDS; wave w of W then takes
 // flat pages [T*w/W, T*(w+1)/W) of the T in all heads, which it walks as one
 // segment per head it touches.  A segment loads its head's query rows once,
-// then streams rounds of pages: a page is served by 8 lanes, load k of lane
-// l reading 16 bytes (4 channels, both bounds) at quad 8k + l % 8 of page
-// l / 8, so each load instruction reads one whole 128-byte line of each of 8
-// neighbouring pages, and a page's sum is 3 DPP levels over its 8 lanes.
-// Rounds are double-buffered: the next round's loads are in flight while
-// the current one is scored; no round past the segment's last is loaded
-// (the test is uniform over the wave).  Inside a round the loads are
-// unconditional: lanes past the segment's end read its last page again,
-// within the same instructions.  The bounds are read with non-temporal loads
-// (each is read once per pass).  The page table is read beside the
-// bounds only to give null pages -inf; pages past a head's end get -inf
-// from a final block-strided fill.  The butterfly order is fixed:
-// deterministic.
+// then streams its pages in double-buffered rounds (score_run).  Pages past
+// a head's end get -inf from a final block-strided fill.
 #include "flat_pages.h"
 #include "kvs_launch.h"
+#include "quest_bound.h"
 
 namespace kvs {
 namespace {
 
 constexpr int kThreads = kFlatThreads;
-
-// Byte selector for v_perm_b32(b, a, sel) with a = (min_c, max_c) and
-// b = (min_c1, max_c1): low half from a (max if q_c >= 0), high half from b.
-__device__ __forceinline__ uint32_t pick_selector(uint32_t q_pair) {
-  const bool pos0 = !(q_pair & 0x8000u), pos1 = !(q_pair & 0x80000000u);
-  const uint32_t lo = pos0 ? 0x0302u : 0x0100u;
-  const uint32_t hi = pos1 ? 0x0706u : 0x0504u;
-  return lo | (hi << 16);
-}
+constexpr int kRing = 2;   // rounds of bounds per wave: one scored, one in flight
 
 // Pages of head rh to score: 0 for a head outside the set.
 __device__ __forceinline__ int page_count(const CacheView& c, const HeadMask& heads, int rh) {
@@ -54,17 +34,13 @@ __device__ __forceinline__ int page_count(const CacheView& c, const HeadMask& he
 template <int D, int GQ, typename DT>
 __global__ __launch_bounds__(kThreads) void score_kernel(CacheView c, const uint16_t* __restrict__ q,
                                                          float* __restrict__ scores, HeadMask heads) {
-  constexpr int LOADS = D / 32;           // 16-byte loads per lane per page
-  constexpr int PPW = 8;                  // pages per step (8 lanes each)
-  constexpr int UNROLL = 8 / LOADS > 0 ? 8 / LOADS : 1;   // steps per round: 32 data registers
-  constexpr int RP = PPW * UNROLL;        // pages per round
   extern __shared__ int pre[];
   __shared__ int part[kThreads];
   const int BH = c.b * c.Hkv;
   page_prefix(BH, [&](int rh) { return page_count(c, heads, rh); }, pre, part);
 
   const int lane = threadIdx.x & 63;
-  const int pp = lane / 8, ql = lane % 8;   // page of the step, lane within the page
+  const int ql = lane % 8;   // lane within the page
   const FlatShare share = flat_share(pre, BH);
   int t0 = share.t0, hh = share.hh;
   const int t1 = share.t1;
@@ -84,64 +60,11 @@ __global__ __launch_bounds__(kThreads) void score_kernel(CacheView c, const uint
     const int64_t mb = c.meta_base[rh];
     float* out = scores + (int64_t)rh * c.maxpg;
 
-    uint32_t qw[GQ][LOADS][2], sel[GQ][LOADS][2];
-#pragma unroll
-    for (int g = 0; g < GQ; ++g) {
-      const uint16_t* qrow = q + ((int64_t)r * c.Hq + h * GQ + g) * D;
-#pragma unroll
-      for (int k = 0; k < LOADS; ++k) {
-        const uint2 v = *reinterpret_cast<const uint2*>(qrow + 4 * (8 * k + ql));
-        qw[g][k][0] = v.x;
-        qw[g][k][1] = v.y;
-        sel[g][k][0] = pick_selector(v.x);
-        sel[g][k][1] = pick_selector(v.y);
-      }
-    }
+    QuestQuery<D, GQ> qq;
+    qq.load(q + ((int64_t)r * c.Hq + h * GQ) * D, ql);
 
-    uint4 mmv[2][UNROLL][LOADS];
-    int ptv[2][UNROLL];
-    auto issue = [&](int rd, uint4 (&dst)[UNROLL][LOADS], int (&pt)[UNROLL]) {
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        const int p = min(p0 + rd * RP + u * PPW + pp, p1 - 1);
-        int64_t m = mb + p;
-        m = m < 0 ? 0 : (m > last ? last : m);
-        const uint16_t* bp = mmb + m * (2 * D);
-#pragma unroll
-        for (int k = 0; k < LOADS; ++k) dst[u][k] = ld16_once(bp + 64 * k);
-        pt[u] = ptrow[p];
-      }
-    };
-    auto score = [&](int rd, const uint4 (&src)[UNROLL][LOADS], const int (&pt)[UNROLL]) {
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        float best = -__builtin_inff();
-#pragma unroll
-        for (int g = 0; g < GQ; ++g) {
-          float acc = 0.f;
-#pragma unroll
-          for (int k = 0; k < LOADS; ++k) {
-            const uint4 v = src[u][k];
-            acc = dot2(qw[g][k][0], __builtin_amdgcn_perm(v.y, v.x, sel[g][k][0]), acc, DT());
-            acc = dot2(qw[g][k][1], __builtin_amdgcn_perm(v.w, v.z, sel[g][k][1]), acc, DT());
-          }
-          best = fmaxf(best, group_sum<8>(acc));
-        }
-        const int p = p0 + rd * RP + u * PPW + pp;
-        const int64_t m = mb + p;
-        const bool present = (pt[u] >= 0 && pt[u] < c.num_pages) || pt[u] == KVS_PAGE_ON_HOST;
-        const bool ok = head_ok && present && m >= 0 && m <= last;
-        if (ql == 0 && p < p1) out[p] = ok ? best : -__builtin_inff();
-      }
-    };
-    const int rounds = (p1 - p0 + RP - 1) / RP;
-    issue(0, mmv[0], ptv[0]);
-    for (int rd = 0; rd < rounds; rd += 2) {   // no round past the segment's last
-      if (rd + 1 < rounds) issue(rd + 1, mmv[1], ptv[1]);
-      score(rd, mmv[0], ptv[0]);
-      if (rd + 2 < rounds) issue(rd + 2, mmv[0], ptv[0]);
-      if (rd + 1 < rounds) score(rd + 1, mmv[1], ptv[1]);
-    }
+    score_run<D, GQ, DT, kRing>(qq, mmb, mb, last, ptrow, c.num_pages, head_ok, p0, p1, lane,
+                         [&](int p, float v) { out[p] = v; });
 
     t0 = seg_end;
     while (hh < BH && uni(pre[hh + 1]) <= t0) ++hh;

@@ -26,7 +26,8 @@ KVS_PAGE_ON_HOST = -2
 # Every symbol include/kvs.h declares.
 EXPORTS = (
     "kvs_build_minmax", "kvs_score_pages", "kvs_score_pages_heads", "kvs_topk_pages",
-    "kvs_topk_pages_heads", "kvs_append_kv", "kvs_prefill_chunk", "kvs_prefill_workspace_bytes",
+    "kvs_topk_pages_heads", "kvs_select_pages", "kvs_append_kv", "kvs_prefill_chunk",
+    "kvs_prefill_workspace_bytes",
     "kvs_offload_pages", "kvs_promote_pages", "kvs_append_kv_tier",
     "kvs_codec_bounds", "kvs_codec_encode", "kvs_codec_decode",
     "kvs_gather_probe", "kvs_gather_probe_sink_words",
@@ -112,6 +113,7 @@ def lib() -> ctypes.CDLL:
         L.kvs_score_pages_heads.argtypes = [pkv, vp, vp, vp, vp]
         L.kvs_topk_pages.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
         L.kvs_topk_pages_heads.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
+        L.kvs_select_pages.argtypes = [pkv, vp, vp, i32, vp, vp, vp]
         L.kvs_append_kv.argtypes = [pkv, vp, vp, vp]
         L.kvs_prefill_chunk.argtypes = [pkv, vp, vp, vp, vp, i32, vp, ctypes.c_size_t, vp]
         L.kvs_prefill_workspace_bytes.argtypes = [i32, i32, i32]
@@ -257,6 +259,20 @@ def kvs_topk_pages(scores: torch.Tensor, seq_len: torch.Tensor, P: int, K: int,
         _check(lib().kvs_topk_pages_heads(_ptr(scores), _ptr(seq_len), P, b, Hkv, max_pages, K,
                                           h.ctypes.data, _ptr(sel), _ptr(sel_count),
                                           _stream(stream)))
+
+
+def kvs_select_pages(cache: Cache, q: torch.Tensor, scores: Optional[torch.Tensor], K: int,
+                     sel: torch.Tensor, sel_count: torch.Tensor, stream=None) -> None:
+    """Scores and top-K of every head in one launch; scores may be None."""
+    s = cache.struct()
+    dev = cache.kv.device
+    _need(q, "q", (s.b, s.Hq, s.d), cache.kv.dtype, dev)
+    if scores is not None:
+        _need(scores, "scores", (s.b, s.Hkv, s.max_group_pages), torch.float32, dev)
+    _need(sel, "sel", (s.b, s.Hkv, K), torch.int32, dev)
+    _need(sel_count, "sel_count", (s.b, s.Hkv), torch.int32, dev)
+    _check(lib().kvs_select_pages(ctypes.byref(s), _ptr(q), _ptr(scores), K, _ptr(sel),
+                                  _ptr(sel_count), _stream(stream)))
 
 
 def kvs_append_kv(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor, stream=None) -> None:

@@ -60,6 +60,20 @@ def topk_cap(wl: Workload) -> float:
     return min(1.0, c.topk * c.P / float(wl.contexts.mean()))
 
 
+def fused_selection(wl: Workload, spread: float = 1.25) -> List[bool]:
+    """Per layer: score and select in one launch (one workgroup per head,
+    kvs_select_pages) when every head of the layer holds pages and the
+    longest holds at most ``spread`` times the mean; otherwise the
+    resident-grid scoring kernel balances the ragged heads and the top-K
+    runs as a launch of its own."""
+    c = wl.cfg
+    if not c.topk:
+        return [False] * c.L
+    npg = -(-wl.n // c.P)
+    return [bool(npg[:, l].min() > 0 and npg[:, l].max() <= spread * npg[:, l].mean())
+            for l in range(c.L)]
+
+
 @dataclass
 class LayerBuffers:
     scores: Optional[torch.Tensor]
@@ -71,7 +85,8 @@ class LayerBuffers:
 class DecodeStep:
     def __init__(self, wl: Workload, device="cuda", T: Optional[int] = None,
                  head_slot: Optional[np.ndarray] = None, S: Optional[np.ndarray] = None,
-                 poison: bool = True, microbatches: int = 1, growth: int = 0):
+                 poison: bool = True, microbatches: int = 1, growth: int = 0,
+                 fused: Optional[bool] = None):
         c = wl.cfg
         self.wl, self.cfg, self.device = wl, c, device
         if head_slot is None:
@@ -93,6 +108,7 @@ class DecodeStep:
                 T = splits_per_request(self.W, c.b, c.G, units)
             S = kvs.kvs_plan_split(wl.budgets, self.head_slot, c.Hp, topk_cap(wl), T)
         self.scale = 1.0 / math.sqrt(c.d)
+        self.fused = fused_selection(wl) if fused is None else [bool(fused and c.topk)] * c.L
         self.set_splits(S, microbatches)
         self.bufs: List[LayerBuffers] = []
         for l in range(c.L):
@@ -128,6 +144,9 @@ class DecodeStep:
     def select(self, l: int, q: torch.Tensor, stream=None) -> None:
         """Score every page of layer l and keep each head's top-K."""
         c, cache, buf = self.cfg, self.caches[l], self.bufs[l]
+        if self.fused[l]:
+            kvs.kvs_select_pages(cache, q, buf.scores, c.topk, buf.sel, buf.sel_count, stream)
+            return
         kvs.kvs_score_pages(cache, q, buf.scores, stream)
         kvs.kvs_topk_pages(buf.scores, cache.seq_len, c.P, c.topk, buf.sel, buf.sel_count, stream)
 
@@ -153,7 +172,10 @@ class DecodeStep:
         r0, r1 = self.parts[k]
         for l in range(c.L):
             cache, buf, q = self.caches[l].rows(r0, r1), self.bufs[l], qs[l][r0:r1]
-            if c.topk:
+            if self.fused[l]:
+                kvs.kvs_select_pages(cache, q, buf.scores[r0:r1], c.topk, buf.sel[r0:r1],
+                                     buf.sel_count[r0:r1], stream)
+            elif c.topk:
                 kvs.kvs_score_pages(cache, q, buf.scores[r0:r1], stream)
                 kvs.kvs_topk_pages(buf.scores[r0:r1], cache.seq_len, c.P, c.topk,
                                    buf.sel[r0:r1], buf.sel_count[r0:r1], stream)
