@@ -230,6 +230,41 @@ def test_append_and_subset_validation():
     assert kvs.last_error()
 
 
+def test_select_validation():
+    """kvs_select_pages checks what kvs_score_pages and kvs_topk_pages check,
+    before any launch (the scores buffer may be NULL)."""
+    L = _lib()
+    s = _FakeCache().s
+    sel, cnt = 0x80000, 0x90000
+    assert L.kvs_select_pages(ctypes.byref(s), None, None, 4, sel, cnt, None) == kvs.KVS_EINVAL
+    assert L.kvs_select_pages(ctypes.byref(s), 0x60008, None, 4, sel, cnt, None) == kvs.KVS_EINVAL
+    assert L.kvs_select_pages(ctypes.byref(s), 0x60000, None, 4, None, cnt, None) == kvs.KVS_EINVAL
+    assert L.kvs_select_pages(ctypes.byref(s), 0x60000, None, 4, sel, None, None) == kvs.KVS_EINVAL
+    for K in (0, 1025):
+        assert L.kvs_select_pages(ctypes.byref(s), 0x60000, None, K, sel, cnt,
+                                  None) == kvs.KVS_EINVAL
+    long_heads = _FakeCache(max_group_pages=8193).s
+    assert L.kvs_select_pages(ctypes.byref(long_heads), 0x60000, None, 4, sel, cnt,
+                              None) == kvs.KVS_EUNSUPPORTED
+    bad = _FakeCache(Hp=3).s
+    assert L.kvs_select_pages(ctypes.byref(bad), 0x60000, None, 4, sel, cnt, None) == kvs.KVS_EINVAL
+    assert L.kvs_select_pages(None, 0x60000, None, 4, sel, cnt, None) == kvs.KVS_EINVAL
+    assert "kvs_select_pages" in kvs.last_error()
+
+
+def test_fused_selection_policy():
+    """One launch only for layers whose heads all hold pages and are of
+    similar length; never without a top-K."""
+    from non_uniform_sparse_amd.pipeline import fused_selection
+    from non_uniform_sparse_amd.workloads import make_workload
+    assert fused_selection(make_workload("flexicache_topk", b=4, N=2048)) == [True]
+    assert not any(fused_selection(make_workload("gemma3_mixed", b=8, L=4)))
+    wl = make_workload("flexicache_topk", b=4, N=2048)
+    wl.n[1, 0, 3] = 0
+    assert fused_selection(wl) == [False]
+    assert not any(fused_selection(make_workload("llama8b_ragged", b=2)))
+
+
 def test_rerank_schedule_matches_oracle():
     from non_uniform_sparse_amd.steps import heads_due
     stable = np.array([True, False, True, True, False, True, True, True])
