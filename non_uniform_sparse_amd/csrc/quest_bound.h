@@ -81,14 +81,15 @@ struct QuestQuery {
 //   mmb     minmax + 8 * ql (elements), the lane's quad of block 0
 //   mb      the head's first metadata block; last: the highest valid block
 //   ptrow   the page-table row of the head's group
-template <int D, int GQ, typename DT, int NB, typename Emit>
+//   NB      round buffers; DATA: data registers per round buffer
+template <int D, int GQ, typename DT, int NB, int DATA, typename Emit>
 __device__ __forceinline__ void score_run(const QuestQuery<D, GQ>& qq, const uint16_t* mmb,
                                           int64_t mb, int64_t last, const int32_t* ptrow,
                                           int num_pages, bool head_ok, int p0, int p1, int lane,
                                           Emit emit) {
   constexpr int LOADS = D / 32;
   constexpr int PPW = 8;                                  // pages per step (8 lanes each)
-  constexpr int UNROLL = 8 / LOADS > 0 ? 8 / LOADS : 1;   // steps per round: 32 data registers
+  constexpr int UNROLL = DATA / (4 * LOADS) > 0 ? DATA / (4 * LOADS) : 1;   // steps per round
   constexpr int RP = PPW * UNROLL;                        // pages per round
   const int pp = lane / 8, ql = lane % 8;
   uint4 mmv[NB][UNROLL][LOADS];

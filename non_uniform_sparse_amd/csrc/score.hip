@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kThreads) void score_kernel(CacheView c, const uint
     QuestQuery<D, GQ> qq;
     qq.load(q + ((int64_t)r * c.Hq + h * GQ) * D, ql);
 
-    score_run<D, GQ, DT, kRing>(qq, mmb, mb, last, ptrow, c.num_pages, head_ok, p0, p1, lane,
+    score_run<D, GQ, DT, kRing, 32>(qq, mmb, mb, last, ptrow, c.num_pages, head_ok, p0, p1, lane,
                          [&](int p, float v) { out[p] = v; });
 
     t0 = seg_end;

@@ -22,6 +22,7 @@ constexpr int P = 16;
 // Rounds of bounds per wave: one scored, one in flight (deeper rings measured
 // slower here).
 constexpr int kRing = 2;
+constexpr int kRoundRegs = 32;   // 64 and 128 measured slower
 
 template <int D, int GQ, typename DT>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(CacheView c,
@@ -50,7 +51,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(CacheView c,
   if (p0 < p1) {
     QuestQuery<D, GQ> qq;
     qq.load(q + ((int64_t)r * c.Hq + h * GQ) * D, ql);
-    score_run<D, GQ, DT, kRing>(qq, mmb, mb, last, ptrow, c.num_pages, head_ok, p0, p1, lane,
+    score_run<D, GQ, DT, kRing, kRoundRegs>(qq, mmb, mb, last, ptrow, c.num_pages, head_ok, p0, p1, lane,
                          [&](int p, float v) {
                            keys[p] = order_key(v);
                            if (srow) srow[p] = v;
