@@ -199,7 +199,10 @@ int kvs_topk_pages_heads(const float* scores, const int32_t* seq_len, int32_t P,
  *              kvs_score_pages writes it, or NULL: the scores are not stored.
  *   K          1 <= K <= 1024.  max_group_pages <= 8192.
  *   sel, sel_count  as kvs_topk_pages.
- * Errors: as the two calls it replaces; nothing is launched on an error.
+ * Errors: the descriptor, q, K and max_group_pages checks of the two calls
+ * it replaces (KVS_EINVAL, KVS_EUNSUPPORTED), except the scoring's b*Hkv
+ * limit, which does not apply (one workgroup per head, no page-count scan);
+ * a launch failure gives KVS_EHIP.  Nothing is launched on an error.
  */
 int kvs_select_pages(const kvs_paged_kv* cache, const void* q, float* scores, int32_t K,
                      int32_t* sel, int32_t* sel_count, void* stream);
