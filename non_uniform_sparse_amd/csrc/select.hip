@@ -25,11 +25,9 @@ constexpr int kRing = 2;
 constexpr int kRoundRegs = 32;   // 64 and 128 measured slower
 
 template <int D, int GQ, typename DT>
-__global__ __launch_bounds__(kSelThreads) void select_kernel(CacheView c,
-                                                             const uint16_t* __restrict__ q,
-                                                             float* __restrict__ scores, int K,
-                                                             int32_t* __restrict__ sel,
-                                                             int32_t* __restrict__ sel_count) {
+__global__ __launch_bounds__(kSelThreads) void select_pages_kernel(
+    CacheView c, const uint16_t* __restrict__ q, float* __restrict__ scores, int K,
+    int32_t* __restrict__ sel, int32_t* __restrict__ sel_count) {
   extern __shared__ uint32_t keys[];   // [maxpg]
   __shared__ SelectShared sh;
   const int rh = blockIdx.x;
@@ -72,8 +70,9 @@ template <int D, int GQ, typename DT>
 hipError_t launch_v(const CacheView& c, const void* q, float* scores, int K, int32_t* sel,
                     int32_t* sel_count, hipStream_t s) {
   const size_t lds = (size_t)c.maxpg * sizeof(uint32_t);
-  hipLaunchKernelGGL((select_kernel<D, GQ, DT>), dim3((unsigned)(c.b * c.Hkv)), dim3(kSelThreads),
-                     lds, s, c, static_cast<const uint16_t*>(q), scores, K, sel, sel_count);
+  hipLaunchKernelGGL((select_pages_kernel<D, GQ, DT>), dim3((unsigned)(c.b * c.Hkv)),
+                     dim3(kSelThreads), lds, s, c, static_cast<const uint16_t*>(q), scores, K, sel,
+                     sel_count);
   return hipGetLastError();
 }
 
