@@ -59,6 +59,9 @@ class DecodeLoop:
         self.stable = (wl.stable_heads(unstable_frac) if stable is None
                        else np.array(stable, dtype=bool))       # [L][Hkv]
         self.n0 = [cache.seq_len.clone() for cache in self.ds.caches]
+        # the bounds as built: an append merges its token into its page's
+        # bounds, so a rewind has to restore them as well as the lengths
+        self.mm0 = [cache.minmax.clone() for cache in self.ds.caches]
         # every step's inputs, resident on the device before any step runs
         qs = [wl.step_qs(steps, l, device) for l in range(c.L)]
         self.q = [[qs[l][t] for l in range(c.L)] for t in range(steps)]
@@ -69,11 +72,12 @@ class DecodeLoop:
 
     def rewind(self) -> None:
         """Back to the state before step 0: the tokens each head held when the
-        caches were built.  Re-running the same steps rewrites the same tokens
-        and bounds (the in-place min/max merge of a token already merged is a
-        no-op), so a rewound replay repeats the first one exactly."""
-        for cache, n0 in zip(self.ds.caches, self.n0):
+        caches were built and the bounds of their pages.  Re-running the same
+        steps rewrites the same tokens, so every step of a rewound replay sees
+        exactly the state the same step saw the first time."""
+        for cache, n0, mm0 in zip(self.ds.caches, self.n0, self.mm0):
             cache.seq_len.copy_(n0)
+            cache.minmax.copy_(mm0)
 
     def run_layer(self, t: int, l: int, stream=None, reuse: bool = True) -> torch.Tensor:
         c, ds = self.cfg, self.ds

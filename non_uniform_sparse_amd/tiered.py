@@ -168,6 +168,7 @@ class TieredLoop:
         self.gpu_bytes = sum(cc.kv.numel() * cc.kv.element_size() for cc in self.ds.caches)
         self.pt0 = [cc.page_table.clone() for cc in self.ds.caches]
         self.n0 = [cc.seq_len.clone() for cc in self.ds.caches]
+        self.mm0 = [cc.minmax.clone() for cc in self.ds.caches] if append else None
         self.moved = [torch.zeros((c.b, c.Hkv), dtype=torch.int32, device=device)
                       for _ in range(c.L)]
         qs = [wl.step_qs(steps, l, device) for l in range(c.L)]
@@ -216,11 +217,14 @@ class TieredLoop:
 
     def rewind(self) -> None:
         """Back to the state before step 0: no stable-head page resident and,
-        with appends, the tokens each head held when the caches were built
-        (re-running the steps rewrites the same rows and bounds)."""
+        with appends, the tokens each head held when the caches were built and
+        the bounds of their pages (re-running the steps rewrites the same
+        rows)."""
         for l in range(self.cfg.L):
             self.ds.caches[l].page_table.copy_(self.pt0[l])
             self.ds.caches[l].seq_len.copy_(self.n0[l])
+            if self.mm0 is not None:
+                self.ds.caches[l].minmax.copy_(self.mm0[l])
             if self.tiers[l] is not None:
                 self.tiers[l].slot_page.fill_(-1)
 

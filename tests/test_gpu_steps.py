@@ -104,15 +104,34 @@ def test_steps_parity(name, ov, steps, period):
     assert reused > 0 and reselected > 0
 
 
+def _step_state(loop):
+    return [(b.sel.clone(), b.sel_count.clone(), b.scores.clone(), b.out.clone(),
+             cc.minmax.clone(), cc.seq_len.clone()) for b, cc in zip(loop.ds.bufs, loop.ds.caches)]
+
+
 def test_step_window_graph_matches_eager():
-    """A captured window of steps (append, partial reranks, decode) replays to
-    the eager result, twice in a row, each time from the rewound caches."""
+    """A rewound window repeats the first one exactly at every step (the
+    selections, scores, outputs, bounds and lengths after each step; steps
+    that score a page still filling would see the tokens of later steps if
+    a rewind left the bounds behind), and a captured window replays to the
+    eager result, twice in a row, each time from the rewound caches."""
     wl, loop = _loop("gemma3_mixed", dict(b=3, L=2, N=4096, topk=16), 6, 4)
     say("[case] step window graph")
     loop.rewind()
+    first = []
     for t in range(6):
         loop.run_step(t)
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        first.append(_step_state(loop))
+    loop.rewind()
+    for t in range(6):
+        loop.run_step(t)
+        torch.cuda.synchronize()
+        for l, (want, got) in enumerate(zip(first[t], _step_state(loop))):
+            for name, a, b in zip(("sel", "sel_count", "scores", "out", "minmax", "seq_len"),
+                                  want, got):
+                assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), \
+                    f"rewound step {t} layer {l}: {name} differs"   # bits: blocks past n hold NaN
     ref = [o.clone() for o in loop.outputs()]
     ref_sel = [b.sel.clone() for b in loop.ds.bufs]
     ref_len = [cc.seq_len.clone() for cc in loop.ds.caches]

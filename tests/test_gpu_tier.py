@@ -306,10 +306,25 @@ def test_tier_appends_window_graph():
     wl = make_workload("flexicache_topk", b=3, N=2000, Hp=1)
     say("[case] tier appends window graph")
     tl = TieredLoop(wl, 6, period=3, stable=_stable(wl.cfg), append=True)
+
+    def state():
+        return [(b.sel.clone(), b.out.clone(), cc.minmax.clone(), cc.seq_len.clone(),
+                 cc.page_table.clone()) for b, cc in zip(tl.ds.bufs, tl.ds.caches)]
+
     tl.rewind()
+    first = []
     for t in range(6):
         tl.run_step(t)
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        first.append(state())
+    tl.rewind()
+    for t in range(6):       # a rewound window repeats the first at every step
+        tl.run_step(t)
+        torch.cuda.synchronize()
+        for l, (want, got) in enumerate(zip(first[t], state())):
+            for name, a, b in zip(("sel", "out", "minmax", "seq_len", "page_table"), want, got):
+                assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), \
+                    f"rewound step {t} layer {l}: {name} differs"   # bits: blocks past n hold NaN
     ref_out = [o.clone() for o in tl.outputs()]
     ref_len = [cc.seq_len.clone() for cc in tl.ds.caches]
     g = tl.capture(6)

@@ -14,6 +14,7 @@ import torch
 import oracle as O
 from non_uniform_sparse_amd import kvs
 from non_uniform_sparse_amd.layout import build_caches, unpack_head
+from non_uniform_sparse_amd.pipeline import splits_per_request
 from non_uniform_sparse_amd.workloads import make_workload
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -108,6 +109,11 @@ def test_plan_split_matches_oracle_random():
         assert got.tolist() == want.tolist()
 
 
+# splits per request of each workload's step on MI355X (as the bench logs them)
+RUNNING_T = {"tiny_ragged": 284, "llama8b_ragged": 128, "flexicache_topk": 51,
+             "longctx_skew": 512, "gemma3_mixed": 32}
+
+
 @pytest.mark.parametrize("name", ["tiny_ragged", "llama8b_ragged", "flexicache_topk",
                                   "longctx_skew", "gemma3_mixed"])
 def test_plan_split_matches_oracle_on_workloads(name):
@@ -117,7 +123,14 @@ def test_plan_split_matches_oracle_on_workloads(name):
     hs = kvs.kvs_cluster_heads(wl.budgets, c.Hp) if c.clustered else \
         np.tile(np.arange(c.Hkv, dtype=np.int32), (c.L, 1))
     cap = c.topk * c.P / float(wl.contexts.mean()) if c.topk else 0.0
-    for T in (c.G, 7, 64, 1024):
+    # the splits per request each workload runs with: T from the rule the
+    # step uses, with W = 2048 concurrent decode workgroups (MI355X: 256
+    # compute units x 8 resident one-wave workgroups for every kernel
+    # variant these workloads build), then halved and doubled
+    units = (np.minimum(c.topk, -(-wl.n // c.P)) if c.topk else -(-wl.n // c.P))
+    T_run = splits_per_request(2048, c.b, c.G, float(units.sum(axis=2).mean()))
+    assert T_run == RUNNING_T[name]
+    for T in (c.G, 7, 64, 1024, T_run, max(c.G, T_run // 2), 2 * T_run):
         T = max(T, c.G)
         assert kvs.kvs_plan_split(wl.budgets, hs, c.Hp, cap, T).tolist() == \
             O.plan_split(wl.budgets, hs, c.Hp, cap, T).tolist()
