@@ -390,6 +390,30 @@ int kvs_decode_attn(const kvs_paged_kv* cache, const void* q, const int32_t* sel
                     const int32_t* sel_count, int32_t K, const int32_t* S_row, float scale,
                     void* workspace, size_t ws_bytes, float* out, void* stream);
 
+/*
+ * kvs_decode_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and results, with the workspace taken from scratch memory
+ * the library holds instead of a caller argument.  Allocates nothing: no
+ * hipMalloc, hipFree or allocating library call.  The caller still passes
+ * the inputs and `out` as for kvs_decode_attn.
+ *   Scratch: one array of KVS_NOALLOC_SCRATCH_BYTES (64 MiB) per device,
+ *   a file-scope device array of the library, present from the library's
+ *   load until the process ends.  Its device address is looked up on the
+ *   first call on each device (the only HIP call besides the launches).
+ *   A shape and split row whose kvs_decode_workspace_bytes exceeds it is
+ *   rejected with KVS_ENOSPC before anything runs (e.g. 64 requests x 16
+ *   query heads x head_dim 256 allow up to 63 splits per group).
+ *   Every call on a device shares that device's array and leaves its last
+ *   contents there (nothing in it needs to start at any value): calls that
+ *   overlap on one device -- on different streams or host threads -- race
+ *   and must be ordered by the caller.
+ */
+#define KVS_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int kvs_decode_attn_noalloc(const kvs_paged_kv* cache, const void* q, const int32_t* sel,
+                            const int32_t* sel_count, int32_t K, const int32_t* S_row,
+                            float scale, float* out, void* stream);
+
 /* Bytes of workspace kvs_decode_attn needs for this shape and split row
  * (per-split partial outputs and log-sum-exps, and each head's first and
  * last split).  0 on bad arguments. */

@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kvs_internal.h"
 #include "kvs_launch.h"
 
@@ -431,38 +433,42 @@ extern "C" size_t kvs_decode_workspace_bytes(int32_t b, int32_t Hq, int32_t Hkv,
 #endif
 }
 
-extern "C" int kvs_decode_attn(const kvs_paged_kv* cache, const void* q, const int32_t* sel,
-                               const int32_t* sel_count, int32_t K, const int32_t* S_row,
-                               float scale, void* workspace, size_t ws_bytes, float* out,
-                               void* stream) {
-  clear_error();
-  const char* fn = "kvs_decode_attn";
-  DecodeArgs a;
-  memset(&a, 0, sizeof a);
-  if (int rc = check_cache(cache, false, fn, &a.c)) return rc;
-  if (!q || !out || !workspace) return set_error(KVS_EINVAL, "%s: null q, out or workspace", fn);
-  if (!aligned16(q) || !aligned16(out) || ((uintptr_t)workspace & 255u))
-    return set_error(KVS_EINVAL, "%s: q/out need 16-byte and workspace 256-byte alignment", fn);
+namespace {
+// Validates the decode's arguments other than the workspace, fills *a (all
+// but the workspace pointers) and the workspace bytes it needs.
+int decode_prepare(const kvs_paged_kv* cache, const void* q, const int32_t* sel,
+                   const int32_t* sel_count, int32_t K, const int32_t* S_row, float scale,
+                   float* out, const char* fn, DecodeArgs* a, size_t* need, size_t* stamps_at) {
+  memset(a, 0, sizeof *a);
+  if (int rc = check_cache(cache, false, fn, &a->c)) return rc;
+  if (!q || !out) return set_error(KVS_EINVAL, "%s: null q or out", fn);
+  if (!aligned16(q) || !aligned16(out))
+    return set_error(KVS_EINVAL, "%s: q and out need 16-byte alignment", fn);
   if (sel && (!sel_count || K < 1 || K > kMaxK))
     return set_error(KVS_EINVAL, "%s: with sel, need sel_count and 1 <= K <= %d", fn, kMaxK);
   if (!(scale > 0.f) || !(scale < 1e30f)) return set_error(KVS_EINVAL, "%s: bad scale", fn);
   int smax = 0;
-  if (int rc = check_splits(S_row, a.c.G, a.c.b, &a, &smax, fn)) return rc;
-  size_t need = workspace_bytes(a.c.b, a.c.Hq, a.c.Hkv, a.c.d, smax);
+  if (int rc = check_splits(S_row, a->c.G, a->c.b, a, &smax, fn)) return rc;
+  *need = workspace_bytes(a->c.b, a->c.Hq, a->c.Hkv, a->c.d, smax);
+  *stamps_at = *need;
 #ifdef KVS_WG_STAMPS
-  const size_t stamps_at = need;
-  need += stamp_bytes(a.c.b, a.splits_total);
+  *need += stamp_bytes(a->c.b, a->splits_total);
 #endif
-  if (ws_bytes < need)
-    return set_error(KVS_ENOSPC, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
-  a.q = q;
-  a.sel = sel;
-  a.sel_count = sel_count;
-  a.K = sel ? K : 0;
-  a.scale_log2 = scale * kLog2e;
-  a.Smax = smax;
+  a->q = q;
+  a->sel = sel;
+  a->sel_count = sel_count;
+  a->K = sel ? K : 0;
+  a->scale_log2 = scale * kLog2e;
+  a->Smax = smax;
+  a->out = out;
+  return KVS_OK;
+}
+
+// Carves the workspace (256-byte aligned, large enough) and launches the
+// split kernel and the combine.
+int decode_launch(DecodeArgs& a, void* workspace, size_t stamps_at, hipStream_t s) {
   char* ws = static_cast<char*>(workspace);
-  const size_t rows = (size_t)a.c.b * a.c.Hq * smax;
+  const size_t rows = (size_t)a.c.b * a.c.Hq * a.Smax;
   a.o_part = reinterpret_cast<float*>(ws);
   ws += round256(rows * a.c.d * sizeof(float));
   a.lse_part = reinterpret_cast<float*>(ws);
@@ -472,12 +478,87 @@ extern "C" int kvs_decode_attn(const kvs_paged_kv* cache, const void* q, const i
   a.split_hi = reinterpret_cast<int32_t*>(ws);
 #ifdef KVS_WG_STAMPS
   a.stamps = reinterpret_cast<uint64_t*>(static_cast<char*>(workspace) + stamps_at);
+#else
+  (void)stamps_at;
 #endif
-  a.out = out;
-  hipStream_t s = (hipStream_t)stream;
   if (hipError_t e = launch_decode(a, s)) return hip_error(e, "kvs_decode_attn (split kernel)");
   if (hipError_t e = launch_combine(a, s)) return hip_error(e, "kvs_decode_attn (combine kernel)");
   return KVS_OK;
+}
+}  // namespace
+
+extern "C" int kvs_decode_attn(const kvs_paged_kv* cache, const void* q, const int32_t* sel,
+                               const int32_t* sel_count, int32_t K, const int32_t* S_row,
+                               float scale, void* workspace, size_t ws_bytes, float* out,
+                               void* stream) {
+  clear_error();
+  const char* fn = "kvs_decode_attn";
+  DecodeArgs a;
+  size_t need = 0, stamps_at = 0;
+  if (int rc = decode_prepare(cache, q, sel, sel_count, K, S_row, scale, out, fn, &a, &need,
+                              &stamps_at))
+    return rc;
+  if (!workspace || ((uintptr_t)workspace & 255u))
+    return set_error(KVS_EINVAL, "%s: workspace must be non-null and 256-byte aligned", fn);
+  if (ws_bytes < need)
+    return set_error(KVS_ENOSPC, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
+  return decode_launch(a, workspace, stamps_at, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------------------
+// kvs_decode_attn without a caller workspace, for callers that cannot
+// allocate device memory.  Its scratch is this file-scope device array:
+// every device the library runs on holds its own copy, from the first use
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory, so the host never passes it to a kernel: the device
+// address of each device's copy comes from hipGetSymbolAddress, taken once
+// per device with that device current, and only that address is used.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[KVS_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_of[kMaxScratchDevices];
+
+// The current device's copy of `scratch` (its address looked up once).
+int noalloc_scratch(void** ptr, const char* fn) {
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev)) return hip_error(e, fn);
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return set_error(KVS_EUNSUPPORTED, "%s: device %d >= %d", fn, dev, kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_of[dev]) {
+    void* p = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) return hip_error(e, fn);
+    if (!p || ((uintptr_t)p & 255u))
+      return set_error(KVS_EHIP, "%s: no aligned device address for the scratch array", fn);
+    g_scratch_of[dev] = p;
+  }
+  *ptr = g_scratch_of[dev];
+  return KVS_OK;
+}
+}  // namespace
+
+extern "C" int kvs_decode_attn_noalloc(const kvs_paged_kv* cache, const void* q,
+                                       const int32_t* sel, const int32_t* sel_count, int32_t K,
+                                       const int32_t* S_row, float scale, float* out,
+                                       void* stream) {
+  clear_error();
+  const char* fn = "kvs_decode_attn_noalloc";
+  DecodeArgs a;
+  size_t need = 0, stamps_at = 0;
+  if (int rc = decode_prepare(cache, q, sel, sel_count, K, S_row, scale, out, fn, &a, &need,
+                              &stamps_at))
+    return rc;
+  if (need > (size_t)KVS_NOALLOC_SCRATCH_BYTES)
+    return set_error(KVS_ENOSPC,
+                     "%s: this shape and split row need %zu bytes of scratch, more than the "
+                     "%zu the library holds per device; use kvs_decode_attn with a workspace",
+                     fn, need, (size_t)KVS_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (int rc = noalloc_scratch(&ws, fn)) return rc;
+  return decode_launch(a, ws, stamps_at, (hipStream_t)stream);
 }
 
 extern "C" int kvs_decode_concurrency(int32_t device, int32_t d, int32_t gqa, int32_t dtype,

@@ -32,7 +32,7 @@ EXPORTS = (
     "kvs_codec_bounds", "kvs_codec_encode", "kvs_codec_decode",
     "kvs_gather_probe", "kvs_gather_probe_sink_words",
     "kvs_plan_split",
-    "kvs_decode_attn",
+    "kvs_decode_attn", "kvs_decode_attn_noalloc",
     "kvs_decode_workspace_bytes", "kvs_decode_concurrency", "kvs_cluster_heads",
     "kvs_last_error",
 )
@@ -131,6 +131,7 @@ def lib() -> ctypes.CDLL:
         L.kvs_gather_probe_sink_words.argtypes = [i32, ctypes.POINTER(i32)]
         L.kvs_plan_split.argtypes = [vp, vp, i32, i32, i32, f64, i32, vp]
         L.kvs_decode_attn.argtypes = [pkv, vp, vp, vp, i32, vp, f32, vp, ctypes.c_size_t, vp, vp]
+        L.kvs_decode_attn_noalloc.argtypes = [pkv, vp, vp, vp, i32, vp, f32, vp, vp]
         L.kvs_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, vp, i32]
         L.kvs_decode_workspace_bytes.restype = ctypes.c_size_t
         L.kvs_decode_concurrency.argtypes = [i32, i32, i32, i32, vp]
@@ -511,6 +512,30 @@ def kvs_decode_attn(cache: Cache, q: torch.Tensor, sel: Optional[torch.Tensor],
     _check(lib().kvs_decode_attn(ctypes.byref(s), _ptr(q), _ptr(sel), _ptr(sel_count), int(K),
                                  S.ctypes.data, float(scale), _ptr(workspace), nbytes, _ptr(out),
                                  _stream(stream)))
+
+
+# Bytes of scratch the library holds per device for kvs_decode_attn_noalloc.
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
+
+
+def kvs_decode_attn_noalloc(cache: Cache, q: torch.Tensor, sel: Optional[torch.Tensor],
+                            sel_count: Optional[torch.Tensor], K: int, S_row: Sequence[int],
+                            scale: float, out: torch.Tensor, stream=None) -> None:
+    """kvs_decode_attn with the library's own per-device scratch instead of a
+    workspace: allocates nothing.  Calls overlapping on one device race."""
+    s = cache.struct()
+    dev = cache.kv.device
+    _need(q, "q", (s.b, s.Hq, s.d), cache.kv.dtype, dev)
+    _need(out, "out", (s.b, s.Hq, s.d), torch.float32, dev)
+    if sel is not None:
+        _need(sel, "sel", (s.b, s.Hkv, K), torch.int32, dev)
+        _need(sel_count, "sel_count", (s.b, s.Hkv), torch.int32, dev)
+    S = np.ascontiguousarray(S_row, dtype=np.int32)
+    if S.shape != (s.Hkv // s.Hp,):
+        raise ValueError(f"S_row must have one entry per group ({s.Hkv // s.Hp})")
+    _check(lib().kvs_decode_attn_noalloc(ctypes.byref(s), _ptr(q), _ptr(sel), _ptr(sel_count),
+                                         int(K), S.ctypes.data, float(scale), _ptr(out),
+                                         _stream(stream)))
 
 
 def kvs_decode_concurrency(device: int, d: int, gqa: int, dtype: torch.dtype) -> int:

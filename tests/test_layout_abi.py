@@ -189,6 +189,30 @@ def test_decode_validation():
     assert L.kvs_decode_attn(*args(q=0)) == kvs.KVS_EINVAL
 
 
+def test_decode_noalloc_validation():
+    """The no-allocation decode makes the same checks as kvs_decode_attn and
+    rejects a shape whose workspace exceeds its per-device scratch, all
+    before any HIP call."""
+    L = _lib()
+    S = np.array([2, 2], dtype=np.int32)
+    args = lambda s, **k: [ctypes.byref(s), k.get("q", 0x60000), k.get("sel", None),
+                           k.get("cnt", None), k.get("K", 0), k.get("S", S).ctypes.data,
+                           ctypes.c_float(k.get("scale", 0.088)), k.get("out", 0x80000), None]
+    s = _FakeCache().s
+    assert L.kvs_decode_attn_noalloc(*args(s, S=np.array([2, 0], dtype=np.int32))) == kvs.KVS_EINVAL
+    assert L.kvs_decode_attn_noalloc(*args(s, sel=0x90000, cnt=None, K=4)) == kvs.KVS_EINVAL
+    assert L.kvs_decode_attn_noalloc(*args(s, scale=-1.0)) == kvs.KVS_EINVAL
+    assert L.kvs_decode_attn_noalloc(*args(s, q=0)) == kvs.KVS_EINVAL
+    assert L.kvs_decode_attn_noalloc(*args(s, out=0x80008)) == kvs.KVS_EINVAL
+    # 64 requests x 16 query heads x d = 256: 63 splits per group fit, 64 do not
+    big = _FakeCache(b=64, Hq=16, Hkv=8, Hp=4, d=256).s
+    fits = kvs.kvs_decode_workspace_bytes(64, 16, 8, 256, np.array([63, 1], dtype=np.int32))
+    over = kvs.kvs_decode_workspace_bytes(64, 16, 8, 256, np.array([64, 1], dtype=np.int32))
+    assert fits <= kvs.NOALLOC_SCRATCH_BYTES < over
+    rc = L.kvs_decode_attn_noalloc(*args(big, S=np.array([64, 1], dtype=np.int32)))
+    assert rc == kvs.KVS_ENOSPC and "scratch" in kvs.last_error()
+
+
 def test_topk_validation():
     L = _lib()
     ok = [0x1000, 0x2000, 16, 1, 8, 640, 64, 0x3000, 0x4000, None]
