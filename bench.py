@@ -108,13 +108,24 @@ def cpu_baseline(wl, step, budget_s: float = 12.0) -> dict:
     scale = 1.0 / math.sqrt(c.d)
     done_bytes, spent, heads = 0, 0.0, 0
     order = [(r, l, h) for l in range(c.L) for r in range(c.b) for h in range(c.Hkv)]
+    # a workload the oracle finishes quickly is passed over again until the
+    # budget is spent, so the figure is not one short, noisy timing
+    passes = max(1, int(budget_s / 0.05))
+    order = (order * passes)[:max(len(order), 200000)]
+    kv_cache = {}
+    keep = int(wl.n.sum()) * c.d * 16 <= 2e9     # the fp64 K and V of every head fit in 2 GB
     for r, l, h in order:
         if l not in q:
             q[l] = wl.q(l, device=step.device).double().cpu().numpy()
         pos = int(step.head_slot[l, h])
-        K, V = wl.head_kv(r, l, h, pos, device=step.device)
-        K, V = K.double().cpu().numpy(), V.double().cpu().numpy()
-        lo, hi = O.page_minmax(K, c.P)
+        if (r, l, h) in kv_cache:
+            K, V, lo, hi = kv_cache[(r, l, h)]
+        else:
+            K, V = wl.head_kv(r, l, h, pos, device=step.device)
+            K, V = K.double().cpu().numpy(), V.double().cpu().numpy()
+            lo, hi = O.page_minmax(K, c.P)
+            if keep:                # a small workload: keep its heads for the next pass
+                kv_cache[(r, l, h)] = (K, V, lo, hi)
         qg = q[l][r, h * c.Gq:(h + 1) * c.Gq]
         t0 = time.perf_counter()
         if c.topk:
@@ -132,7 +143,8 @@ def cpu_baseline(wl, step, budget_s: float = 12.0) -> dict:
     limiter.restore_original_limits()
     return {"value": done_bytes / spent / 1e9, "unit": "GB/s", "cores": int(cores),
             "kind": "oracle",
-            "sample": f"{heads} whole heads (request-major from layer 0) of {c.name}, "
+            "sample": f"{heads} whole heads (request-major from layer 0, the workload passed "
+                      f"over again while time was left) of {c.name}, "
                       f"{done_bytes / 1e6:.1f} MB of KV in {spent:.1f} s; BLAS threads = "
                       f"cores = {cores} (the host's affinity set); the oracle's loop over "
                       "heads and pages is itself sequential"}
@@ -482,46 +494,83 @@ def codec_report(name: str = "llama7b_chunk", reps: int = 10) -> dict:
     }
 
 
-def skew_report(configs, launches: int = 20) -> dict:
-    """Per-workgroup duration skew of the split-K decode kernel, max / mean
-    over the workgroups of one launch, median over launches, per layer; with
+def skew_report(configs, launches: int = 20, T=None) -> dict:
+    """Per-workgroup duration skew of the split-K decode kernel (max / mean
+    over the workgroups of one launch, median over launches, per layer) and
+    the launch's duration (HIP events, median over launches, per layer), with
     the planned split map and with a uniform one of the same total (equal
-    budgets).  Uses the stamp-instrumented library build."""
+    budgets).  The launches of a layer are queued back to back behind a GPU
+    spin, each followed by a copy of its stamps.  Uses the stamp-instrumented
+    library build (each workgroup records its start and end)."""
     from non_uniform_sparse_amd import build as B
     kvs.use_library(B.LIB_STAMPS)
     out = {}
     for name in configs:
         wl = make_workload(name)
         c = wl.cfg
-        step = DecodeStep(wl, device="cuda:0")
+        step = DecodeStep(wl, device="cuda:0", T=T)
         qs = step.queries()
         if c.topk:
             for l in range(c.L):
                 step.select(l, qs[l])
-        res = {}
-        for label in ("planned", "uniform"):
-            per_layer = []
+        stream = torch.cuda.Stream()
+        rate = sleep_rate(stream)
+
+        def row_of(label, l):
+            return step.S[l] if label == "planned" else kvs.kvs_plan_split(
+                np.ones((1, c.Hkv)), step.head_slot[l:l + 1], c.Hp, 0.0, int(step.S[l].sum()))[0]
+        for label in ("planned", "uniform"):           # warm-up: every layer, both maps
             for l in range(c.L):
-                T = int(step.S[l].sum())
-                row = step.S[l] if label == "planned" else kvs.kvs_plan_split(
-                    np.ones((1, c.Hkv)), step.head_slot[l:l + 1], c.Hp, 0.0, T)[0]
+                row = row_of(label, l)
                 need = kvs.kvs_decode_workspace_bytes(c.b, c.Hq, c.Hkv, c.d, row)
                 if need > step.workspace.numel():
                     step.workspace = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+                step.attend(l, qs[l], stream, S_row=row)
+        stream.synchronize()
+        res = {}
+        for label in ("planned", "uniform"):
+            skew_l, us_l, xcd_l = [], [], []
+            for l in range(c.L):
+                row = row_of(label, l)
                 off = kvs.kvs_decode_stamps_offset(c.b, c.Hq, c.Hkv, c.d, row)
                 nwg = c.b * int(np.sum(row))
-                skews = []
-                for _ in range(launches):
-                    step.attend(l, qs[l], S_row=row)
-                    torch.cuda.synchronize()
-                    st = step.workspace[off:off + nwg * 16].view(torch.int64).view(nwg, 2).cpu()
-                    dur = (st[:, 1] - st[:, 0]).double()
-                    skews.append(float(dur.max() / dur.mean()))
-                per_layer.append(statistics.median(skews))
-            res[label] = {"median_over_layers": round(statistics.median(per_layer), 3),
-                          "max_over_layers": round(max(per_layer), 3),
-                          "per_layer": [round(x, 3) for x in per_layer]}
+                src = step.workspace[off:off + nwg * 16].view(torch.int64).view(nwg, 2)
+                stamps = torch.empty((launches, nwg, 2), dtype=torch.int64, device="cuda:0")
+                marks = []
+                with torch.cuda.stream(stream):   # a spin long enough for the host to enqueue
+                    torch.cuda._sleep(int(rate * (2.0 + 0.5 * launches)))
+                    for i in range(launches):
+                        e0, e1 = torch.cuda.Event(enable_timing=True), \
+                            torch.cuda.Event(enable_timing=True)
+                        e0.record(stream)
+                        step.attend(l, qs[l], stream, S_row=row)
+                        e1.record(stream)
+                        stamps[i].copy_(src)
+                        marks.append((e0, e1))
+                stream.synchronize()
+                dur = (stamps[:, :, 1] - stamps[:, :, 0]).double().cpu()      # [launch][wg]
+                skew_l.append(statistics.median((dur.max(1).values / dur.mean(1)).tolist()))
+                us_l.append(statistics.median(a.elapsed_time(b_) * 1e3 for a, b_ in marks))
+                # workgroups go round-robin over the 8 XCDs: mean duration per XCD
+                xm = dur.view(launches, -1, 8).mean(1) if nwg % 8 == 0 else None
+                if xm is not None:
+                    xcd_l.append(statistics.median((xm.max(1).values / xm.min(1).values).tolist()))
+            worst = int(np.argmax(skew_l))
+            res[label] = {
+                "skew_median_over_layers": round(statistics.median(skew_l), 3),
+                "skew_worst_layer": round(skew_l[worst], 3), "worst_layer": worst,
+                "skew_per_layer": [round(x, 3) for x in skew_l],
+                "decode_us_per_layer": [round(x, 1) for x in us_l],
+                "decode_us_sum": round(sum(us_l), 1),
+                "xcd_mean_duration_max_over_min_median": (round(statistics.median(xcd_l), 3)
+                                                          if xcd_l else None),
+            }
         res["splits_per_request"] = step.T
+        res["uniform_over_planned_decode_us"] = round(
+            res["uniform"]["decode_us_sum"] / res["planned"]["decode_us_sum"], 3)
+        res["note"] = ("skew = max / mean workgroup duration of one launch (s_memrealtime "
+                       "stamps), median over launches; decode_us from HIP events around each "
+                       "launch of the instrumented build (split kernel + combine)")
         out[name] = res
         del step
         torch.cuda.empty_cache()
@@ -572,6 +621,11 @@ def main() -> int:
                          "(default configs: flexicache_topk, gemma3_mixed at 8 layers), print "
                          "that record and exit")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--logits", choices=["mfma", "valu"], default="mfma",
+                    help="decode logits on MFMA (the library) or on the VALU (the measurement "
+                         "build that backs the MFMA choice)")
+    ap.add_argument("--splits", type=int, default=None,
+                    help="splits per request per layer (default: the planned rule)")
     ap.add_argument("--skew", nargs="*", default=None, metavar="CONFIG",
                     help="measure per-workgroup duration skew (planned vs uniform split "
                          "map) with the instrumented build, print it and exit")
@@ -584,6 +638,9 @@ def main() -> int:
               "run with --gpus 1", file=sys.stderr)
         return 2
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.logits == "valu":
+        from non_uniform_sparse_amd import build as B
+        kvs.use_library(B.LIB_VALU)
     dev = "cuda:0"
     torch.cuda.set_device(0)
     if args.prefill is not None:
@@ -605,7 +662,8 @@ def main() -> int:
         print(json.dumps({"tier": tier_report(args.tier)}))
         return 0
     if args.skew is not None:
-        print(json.dumps({"skew": skew_report(args.skew or ["llama8b_ragged", "longctx_skew"])}))
+        print(json.dumps({"skew": skew_report(args.skew or ["llama8b_ragged", "longctx_skew"],
+                                              T=args.splits)}))
         return 0
     if args.copy_probe:
         n = 1 << 30
@@ -627,7 +685,7 @@ def main() -> int:
     t0 = time.time()
     wl = make_workload(args.config)
     c = wl.cfg
-    step = DecodeStep(wl, device=dev,
+    step = DecodeStep(wl, device=dev, T=args.splits,
                       microbatches=args.microbatches or default_microbatches(wl),
                       fused={"auto": None, "on": True, "off": False}[args.fused_select])
     qs = step.queries()

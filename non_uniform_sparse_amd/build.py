@@ -15,6 +15,9 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvs.so")
 # Instrumented variant: decode workgroups record start/end stamps (skew runs only).
 LIB_STAMPS = os.path.join(PKG, "libkvs_stamps.so")
+# Measurement variant: the decode's logits on the VALU instead of MFMA (the
+# comparison behind the MFMA choice; bench.py --logits valu).
+LIB_VALU = os.path.join(PKG, "libkvs_valu.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -61,9 +64,11 @@ def build(verbose: bool = False, csrc: str = CSRC, lib: str = LIB,
 
 
 def build_all(verbose: bool = False) -> None:
-    """The library and its workgroup-stamp instrumented variant."""
+    """The library, its workgroup-stamp instrumented variant and its
+    VALU-logits measurement variant."""
     build(verbose)
     build(verbose, lib=LIB_STAMPS, build_dir=BUILD + "_stamps", defines=("-DKVS_WG_STAMPS",))
+    build(verbose, lib=LIB_VALU, build_dir=BUILD + "_valu", defines=("-DKVS_VALU_LOGITS",))
 
 
 if __name__ == "__main__":

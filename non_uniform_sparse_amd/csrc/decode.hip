@@ -30,6 +30,16 @@
 namespace kvs {
 namespace {
 
+// Measurement build only (libkvs_valu.so): the page's logits as VALU
+// pair-dot products summed across each row's lanes instead of MFMA, the
+// rest of the kernel unchanged -- the comparison that justifies MFMA for
+// the query group's logits.
+#ifdef KVS_VALU_LOGITS
+constexpr bool kValuLogits = true;
+#else
+constexpr bool kValuLogits = false;
+#endif
+
 template <int D, int GQ, typename DT>
 __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   using Geo = Geometry<D>;
@@ -107,6 +117,8 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   uint4 qop[KB];            // Q^T operand of the current head
   float m_col, l_col;       // running max / partial sum of column rcol's head
   float o[GQ][8];           // V-side accumulators
+  uint32_t qv[GQ][4];       // VALU logits only: this lane's 8 channels of each query row
+  float m_v[GQ], l_v[GQ];   // VALU logits only: running max / partial sum per query row
   int cur_j = -1;
 
   auto begin_head = [&](int j) {
@@ -126,15 +138,35 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     for (int g = 0; g < GQ; ++g)
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[g][e] = 0.f;
+    if constexpr (kValuLogits) {
+#pragma unroll
+      for (int g = 0; g < GQ; ++g) {
+        const uint4 v = ld16(qb + ((int64_t)r * c.Hq + h * GQ + g) * D + 8 * vcol);
+        qv[g][0] = v.x;
+        qv[g][1] = v.y;
+        qv[g][2] = v.z;
+        qv[g][3] = v.w;
+        m_v[g] = -__builtin_inff();
+        l_v[g] = 0.f;
+      }
+    }
   };
   // Merge the row groups and write this split's partial for the head in slot j.
   auto end_head = [&](int j) {
     const int h = gu.head[j];
-    const float lt = across_sum<16>(l_col);   // total over the 4 result row groups
     float lg[GQ], mg[GQ];
-    [&]<int... G>(std::integer_sequence<int, G...>) {
-      ((lg[G] = from_result<D, 0, G>(lt), mg[G] = from_result<D, 0, G>(m_col)), ...);
-    }(std::make_integer_sequence<int, GQ>{});
+    if constexpr (kValuLogits) {
+#pragma unroll
+      for (int g = 0; g < GQ; ++g) {
+        lg[g] = across_sum<COLS>(l_v[g]);   // total over the V row groups
+        mg[g] = m_v[g];
+      }
+    } else {
+      const float lt = across_sum<16>(l_col);   // total over the 4 result row groups
+      [&]<int... G>(std::integer_sequence<int, G...>) {
+        ((lg[G] = from_result<D, 0, G>(lt), mg[G] = from_result<D, 0, G>(m_col)), ...);
+      }(std::make_integer_sequence<int, GQ>{});
+    }
 #pragma unroll
     for (int g = 0; g < GQ; ++g)
 #pragma unroll
@@ -222,6 +254,43 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
         }
         return;
       }
+      float cg[GQ], pb[TL][GQ];   // rescale factor per query head, probabilities per V row
+      if constexpr (kValuLogits) {
+        // logits of the lane's rows: pair-dots over its 8 channels, summed
+        // across the row's COLS lanes; softmax in the V layout
+        float z[TL][GQ];
+#pragma unroll
+        for (int k = 0; k < TL; ++k) {
+          const bool ok = rg + RPL * k < valid;
+#pragma unroll
+          for (int g = 0; g < GQ; ++g) {
+            float acc = dot2(qv[g][0], kc[B][k].x, 0.f, DT());
+            acc = dot2(qv[g][1], kc[B][k].y, acc, DT());
+            acc = dot2(qv[g][2], kc[B][k].z, acc, DT());
+            acc = dot2(qv[g][3], kc[B][k].w, acc, DT());
+            acc = group_sum<COLS>(acc);
+            z[k][g] = ok ? acc * a.scale_log2 : -__builtin_inff();
+          }
+        }
+        if (more) load_k(nt, kc[B]);
+#pragma unroll
+        for (int g = 0; g < GQ; ++g) {
+          float tmax = z[0][g];
+#pragma unroll
+          for (int k = 1; k < TL; ++k) tmax = fmaxf(tmax, z[k][g]);
+          tmax = across_max<COLS>(tmax);
+          const float mnew = fmaxf(m_v[g], tmax);
+          cg[g] = __builtin_amdgcn_exp2f(m_v[g] - mnew);
+          m_v[g] = mnew;
+          float psum = 0.f;
+#pragma unroll
+          for (int k = 0; k < TL; ++k) {
+            pb[k][g] = __builtin_amdgcn_exp2f(z[k][g] - mnew);
+            psum += pb[k][g];
+          }
+          l_v[g] = l_v[g] * cg[g] + psum;
+        }
+      } else {
       // K rows -> LDS, then back in MFMA operand layout (the global loads stay
       // whole-row coalesced; the MFMA wants 16 rows x 64 B per operand).
 #pragma unroll
@@ -260,7 +329,6 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
       l_col = l_col * corr + psum;
 
       // broadcast rescale factors and probabilities to the V lanes
-      float cg[GQ], pb[TL][GQ];
       [&]<int... G>(std::integer_sequence<int, G...>) {
         ((cg[G] = from_result<D, 0, G>(corr)), ...);
         [&]<int... HI>(std::integer_sequence<int, HI...>) {
@@ -272,6 +340,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
         }(std::make_integer_sequence<int, TL>{});
       }(std::make_integer_sequence<int, GQ>{});
 
+      }
 #pragma unroll
       for (int g = 0; g < GQ; ++g)
 #pragma unroll

@@ -53,11 +53,14 @@ def default_microbatches(wl: Workload) -> int:
 
 def topk_cap(wl: Workload) -> float:
     """Budget cap for the split weights when a top-K also bounds the work:
-    a head never attends more than K*P tokens, i.e. a budget of K*P / N."""
+    a head never attends more than K*P tokens, i.e. a budget of K*P / N.
+    The map has no request axis, and the longest request of the batch sets
+    the launch's duration, so N is the longest context: the cap is the
+    budget at which a head of that request attends all of its K pages."""
     c = wl.cfg
     if not c.topk:
         return 0.0
-    return min(1.0, c.topk * c.P / float(wl.contexts.mean()))
+    return min(1.0, c.topk * c.P / float(wl.contexts.max()))
 
 
 def fused_selection(wl: Workload, spread: float = 1.25) -> List[bool]:

@@ -14,7 +14,7 @@ import torch
 import oracle as O
 from non_uniform_sparse_amd import kvs
 from non_uniform_sparse_amd.layout import build_caches, unpack_head
-from non_uniform_sparse_amd.pipeline import splits_per_request
+from non_uniform_sparse_amd.pipeline import splits_per_request, topk_cap
 from non_uniform_sparse_amd.workloads import make_workload
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -122,7 +122,7 @@ def test_plan_split_matches_oracle_on_workloads(name):
     c = wl.cfg
     hs = kvs.kvs_cluster_heads(wl.budgets, c.Hp) if c.clustered else \
         np.tile(np.arange(c.Hkv, dtype=np.int32), (c.L, 1))
-    cap = c.topk * c.P / float(wl.contexts.mean()) if c.topk else 0.0
+    cap = topk_cap(wl)
     # the splits per request each workload runs with: T from the rule the
     # step uses, with W = 2048 concurrent decode workgroups (MI355X: 256
     # compute units x 8 resident one-wave workgroups for every kernel
