@@ -30,24 +30,12 @@
 namespace kvs {
 namespace {
 
-// Measurement build only (libkvs_valu.so): the page's logits as VALU
-// pair-dot products summed across each row's lanes instead of MFMA, the
-// rest of the kernel unchanged -- the comparison that justifies MFMA for
-// the query group's logits.
-#ifdef KVS_VALU_LOGITS
-constexpr bool kValuLogits = true;
-#else
-constexpr bool kValuLogits = false;
-#endif
-
 template <int D, int GQ, typename DT>
 __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
-  using Geo = Geometry<D>;
-  constexpr int COLS = Geo::COLS, RPL = Geo::RPL, TL = Geo::TL, A = Geo::A, KB = Geo::KB;
-  static_assert(GQ <= 16, "query group must fit the 16 MFMA columns");
-  constexpr int KROW = D + 8;                 // LDS row stride (halves): 16 B pad
+  using PA = PageAttention<D, GQ, DT>;
+  constexpr int COLS = PA::COLS, TL = PA::TL;
   __shared__ GroupUnits gu;
-  __shared__ uint4 ktile_raw[P * KROW / 8];    // one page's K tile, row-major
+  __shared__ uint4 ktile_raw[PA::KTILE_HALVES / 8];   // one page's K tile, row-major
   uint16_t* ktile = reinterpret_cast<uint16_t*>(ktile_raw);
   const CacheView& c = a.c;
   const int lane = threadIdx.x;
@@ -97,93 +85,33 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
     }
   }
 
-  // V-side role (also how K is fetched: RPL whole rows per load instruction)
-  const int rg = lane / COLS, vcol = lane % COLS;
-  const int v_off = rg * D + 8 * vcol;
-  // MFMA roles: operand row m = lane % 16 (a token), k sub-block kq = lane / 16
-  const int m = lane % 16, kq = lane / 16;
-  const int ka = m / 4, ki = m % 4;
-  const int k_tok = (ka / A) + RPL * (4 * (ka % A) + ki);   // token fed as MFMA row m
-  const int k_lds = k_tok * KROW + 8 * kq;                  // its operand slice in LDS
-  const int w_lds = rg * KROW + 8 * vcol;                   // where this lane stores K rows
-  // result role: column (query head) rcol, row group ra holding 4 tokens
-  const int rcol = lane % 16, ra = lane / 16;
-  const int r_tok0 = (ra / A) + RPL * 4 * (ra % A);          // token of element i: r_tok0 + RPL*i
-
+  PA pa(lane);
   const int32_t* pt = c.page_table + ((int64_t)r * c.G + gi) * c.maxpg;
   const uint16_t* kvb = reinterpret_cast<const uint16_t*>(c.kv);
   const uint16_t* qb = reinterpret_cast<const uint16_t*>(a.q);
-
-  uint4 qop[KB];            // Q^T operand of the current head
-  float m_col, l_col;       // running max / partial sum of column rcol's head
-  float o[GQ][8];           // V-side accumulators
-  uint32_t qv[GQ][4];       // VALU logits only: this lane's 8 channels of each query row
-  float m_v[GQ], l_v[GQ];   // VALU logits only: running max / partial sum per query row
   int cur_j = -1;
 
-  auto begin_head = [&](int j) {
-    const int h = gu.head[j];
-    const bool has = rcol < GQ;
-    // unconditional loads (columns >= GQ read row 0 and are zeroed), so no
-    // branch hides them from the wait-count bookkeeping of the loop
-    const uint16_t* qrow = qb + ((int64_t)r * c.Hq + h * GQ + (has ? rcol : 0)) * D + 8 * kq;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const uint4 v = ld16(qrow + 32 * kb);
-      qop[kb] = has ? v : make_uint4(0, 0, 0, 0);
-    }
-    m_col = -__builtin_inff();
-    l_col = 0.f;
-#pragma unroll
-    for (int g = 0; g < GQ; ++g)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[g][e] = 0.f;
-    if constexpr (kValuLogits) {
-#pragma unroll
-      for (int g = 0; g < GQ; ++g) {
-        const uint4 v = ld16(qb + ((int64_t)r * c.Hq + h * GQ + g) * D + 8 * vcol);
-        qv[g][0] = v.x;
-        qv[g][1] = v.y;
-        qv[g][2] = v.z;
-        qv[g][3] = v.w;
-        m_v[g] = -__builtin_inff();
-        l_v[g] = 0.f;
-      }
-    }
-  };
   // Merge the row groups and write this split's partial for the head in slot j.
   auto end_head = [&](int j) {
     const int h = gu.head[j];
     float lg[GQ], mg[GQ];
-    if constexpr (kValuLogits) {
-#pragma unroll
-      for (int g = 0; g < GQ; ++g) {
-        lg[g] = across_sum<COLS>(l_v[g]);   // total over the V row groups
-        mg[g] = m_v[g];
-      }
-    } else {
-      const float lt = across_sum<16>(l_col);   // total over the 4 result row groups
-      [&]<int... G>(std::integer_sequence<int, G...>) {
-        ((lg[G] = from_result<D, 0, G>(lt), mg[G] = from_result<D, 0, G>(m_col)), ...);
-      }(std::make_integer_sequence<int, GQ>{});
-    }
-#pragma unroll
-    for (int g = 0; g < GQ; ++g)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[g][e] = across_sum<COLS>(o[g][e]);
-    if (rg == 0) {
+    pa.finish(lg, mg);
+    if (pa.rg == 0) {
 #pragma unroll
       for (int g = 0; g < GQ; ++g) {
         const int64_t row = ((int64_t)r * c.Hq + h * GQ + g) * a.Smax + s;
         const bool empty = !(lg[g] > 0.f);
         const float inv = empty ? 0.f : 1.f / lg[g];
-        float4* dst = reinterpret_cast<float4*>(a.o_part + row * D + 8 * vcol);
-        dst[0] = make_float4(o[g][0] * inv, o[g][1] * inv, o[g][2] * inv, o[g][3] * inv);
-        dst[1] = make_float4(o[g][4] * inv, o[g][5] * inv, o[g][6] * inv, o[g][7] * inv);
-        if (vcol == 0) a.lse_part[row] = empty ? -__builtin_inff() : mg[g] + log2f(lg[g]);
+        float4* dst = reinterpret_cast<float4*>(a.o_part + row * D + 8 * pa.vcol);
+        dst[0] = make_float4(pa.o[g][0] * inv, pa.o[g][1] * inv, pa.o[g][2] * inv,
+                             pa.o[g][3] * inv);
+        dst[1] = make_float4(pa.o[g][4] * inv, pa.o[g][5] * inv, pa.o[g][6] * inv,
+                             pa.o[g][7] * inv);
+        if (pa.vcol == 0) a.lse_part[row] = empty ? -__builtin_inff() : mg[g] + log2f(lg[g]);
       }
     }
   };
+  static_assert(COLS * 8 == D, "V lanes cover a row");
 
   // Pages in flight per wave: two for d = 128 (8 KB pages), one for d = 256
   // (16 KB pages), at the same occupancy.
@@ -218,19 +146,11 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
       const int j = __builtin_amdgcn_readlane(my_j, t);
       return kvb + (phys >= 0 ? ((int64_t)phys * c.Hp + j) * 2 * P * D : 0);
     };
-    auto load_k = [&](const uint16_t* kt, uint4 (&dst)[TL]) {
-#pragma unroll
-      for (int k = 0; k < TL; ++k) dst[k] = ld16_once(kt + v_off + RPL * k * D);
-    };
-    auto load_v = [&](const uint16_t* kt, uint4 (&dst)[TL]) {
-#pragma unroll
-      for (int k = 0; k < TL; ++k) dst[k] = ld16_once(kt + P * D + v_off + RPL * k * D);
-    };
 #pragma unroll
     for (int b = 0; b < DEPTH; ++b) {
       const uint16_t* kt = tile(b < nb ? b : nb - 1);
-      load_k(kt, kc[b]);
-      load_v(kt, vr[b]);
+      pa.load_k(kt, kc[b]);
+      pa.load_v(kt, vr[b]);
     }
     // One unit, its tiles in buffer B; refills buffer B with unit t + DEPTH.
     auto unit = [&]<int B>(int t) {
@@ -239,7 +159,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
       const int valid = __builtin_amdgcn_readlane(my_valid, t);
       if (j != cur_j) {
         if (cur_j >= 0) end_head(cur_j);
-        begin_head(j);
+        pa.begin(qb + ((int64_t)r * c.Hq + gu.head[j] * GQ) * D);
         cur_j = j;
       }
       // tile to prefetch; past the batch end there is none (the condition is
@@ -249,119 +169,14 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
       const uint16_t* nt = tile(more ? t + DEPTH : nb - 1);
       if (phys < 0 || valid <= 0) {
         if (more) {
-          load_k(nt, kc[B]);
-          load_v(nt, vr[B]);
+          pa.load_k(nt, kc[B]);
+          pa.load_v(nt, vr[B]);
         }
         return;
       }
-      float cg[GQ], pb[TL][GQ];   // rescale factor per query head, probabilities per V row
-      if constexpr (kValuLogits) {
-        // logits of the lane's rows: pair-dots over its 8 channels, summed
-        // across the row's COLS lanes; softmax in the V layout
-        float z[TL][GQ];
-#pragma unroll
-        for (int k = 0; k < TL; ++k) {
-          const bool ok = rg + RPL * k < valid;
-#pragma unroll
-          for (int g = 0; g < GQ; ++g) {
-            float acc = dot2(qv[g][0], kc[B][k].x, 0.f, DT());
-            acc = dot2(qv[g][1], kc[B][k].y, acc, DT());
-            acc = dot2(qv[g][2], kc[B][k].z, acc, DT());
-            acc = dot2(qv[g][3], kc[B][k].w, acc, DT());
-            acc = group_sum<COLS>(acc);
-            z[k][g] = ok ? acc * a.scale_log2 : -__builtin_inff();
-          }
-        }
-        if (more) load_k(nt, kc[B]);
-#pragma unroll
-        for (int g = 0; g < GQ; ++g) {
-          float tmax = z[0][g];
-#pragma unroll
-          for (int k = 1; k < TL; ++k) tmax = fmaxf(tmax, z[k][g]);
-          tmax = across_max<COLS>(tmax);
-          const float mnew = fmaxf(m_v[g], tmax);
-          cg[g] = __builtin_amdgcn_exp2f(m_v[g] - mnew);
-          m_v[g] = mnew;
-          float psum = 0.f;
-#pragma unroll
-          for (int k = 0; k < TL; ++k) {
-            pb[k][g] = __builtin_amdgcn_exp2f(z[k][g] - mnew);
-            psum += pb[k][g];
-          }
-          l_v[g] = l_v[g] * cg[g] + psum;
-        }
-      } else {
-      // K rows -> LDS, then back in MFMA operand layout (the global loads stay
-      // whole-row coalesced; the MFMA wants 16 rows x 64 B per operand).
-#pragma unroll
-      for (int k = 0; k < TL; ++k)
-        *reinterpret_cast<uint4*>(ktile + w_lds + RPL * k * KROW) = kc[B][k];
-      if (more) load_k(nt, kc[B]);   // K registers free: fetch a later unit's K
-      // The workgroup is one wave and a wave's LDS operations execute in
-      // order; the compiler barrier keeps the reads after the writes and the
-      // LDS-only wait (vmcnt, expcnt left at their maxima) leaves the
-      // prefetch loads in flight.
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      uint4 kr[KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) kr[kb] = *reinterpret_cast<const uint4*>(ktile + k_lds + 32 * kb);
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) acc = mfma16x16x32(kr[kb], qop[kb], acc, DT());
-      // online softmax in the result layout (column rcol = query head)
-      float z[4], tmax = -__builtin_inff();
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        z[i] = r_tok0 + RPL * i < valid ? acc[i] * a.scale_log2 : -__builtin_inff();
-        tmax = fmaxf(tmax, z[i]);
-      }
-      tmax = across_max<16>(tmax);
-      const float mnew = fmaxf(m_col, tmax);
-      const float corr = __builtin_amdgcn_exp2f(m_col - mnew);
-      m_col = mnew;
-      float pr[4], psum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pr[i] = __builtin_amdgcn_exp2f(z[i] - mnew);
-        psum += pr[i];
-      }
-      l_col = l_col * corr + psum;
-
-      // broadcast rescale factors and probabilities to the V lanes
-      [&]<int... G>(std::integer_sequence<int, G...>) {
-        ((cg[G] = from_result<D, 0, G>(corr)), ...);
-        [&]<int... HI>(std::integer_sequence<int, HI...>) {
-          auto one = [&]<int HIV>() {
-            constexpr int HH = HIV / 4, I = HIV % 4;
-            ((pb[4 * HH + I][G] = from_result<D, HH, G>(pr[I])), ...);
-          };
-          (one.template operator()<HI>(), ...);
-        }(std::make_integer_sequence<int, TL>{});
-      }(std::make_integer_sequence<int, GQ>{});
-
-      }
-#pragma unroll
-      for (int g = 0; g < GQ; ++g)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[g][e] *= cg[g];
-#pragma unroll
-      for (int k = 0; k < TL; ++k) {
-        // rows past the valid count hold no token (possibly NaN): zero them
-        const bool ok = rg + RPL * k < valid;
-        const uint32_t w[4] = {ok ? vr[B][k].x : 0u, ok ? vr[B][k].y : 0u,
-                               ok ? vr[B][k].z : 0u, ok ? vr[B][k].w : 0u};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float v0 = lo_f(w[e], DT()), v1 = hi_f(w[e], DT());
-#pragma unroll
-          for (int g = 0; g < GQ; ++g) {
-            o[g][2 * e] += pb[k][g] * v0;
-            o[g][2 * e + 1] += pb[k][g] * v1;
-          }
-        }
-      }
-      if (more) load_v(nt, vr[B]);   // V consumed: fetch a later unit's V
+      pa.page(kc[B], vr[B], valid, ktile, a.scale_log2,
+              [&] { if (more) pa.load_k(nt, kc[B]); },
+              [&] { if (more) pa.load_v(nt, vr[B]); });
     };
     for (int t0 = 0; t0 < nb; t0 += DEPTH) {
       [&]<int... B>(std::integer_sequence<int, B...>) {

@@ -75,9 +75,12 @@ def check_layer(step: DecodeStep, l: int, q: torch.Tensor, requests: Sequence[in
     slots = oracle_slots(wl)
     assert np.array_equal(slots[l], step.head_slot[l]), "clustering differs from the oracle"
     cache, lay = step.caches[l], step.layouts[l]
-    if c.topk:
-        step.select(l, q)
-    out = step.attend(l, q, S_row=S_row)
+    if S_row is None:
+        out = step.run_layer(l, q)          # the path the step takes for this layer
+    else:
+        if c.topk:
+            step.select(l, q)
+        out = step.attend(l, q, S_row=S_row)
     torch.cuda.synchronize()
     q64 = q.double().cpu().numpy()
     out_h = out.cpu().numpy().astype(np.float64)
