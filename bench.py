@@ -811,6 +811,39 @@ def main() -> int:
              for l in range(c.L)]
     pr_bytes = statistics.mean(units) * 2 * c.P * c.d * 2
     pr_gbps = pr_bytes / (pr_ms * 1e-3) / 1e9
+    # Plain contiguous reads of the kernels' own byte counts (no gather, no
+    # arithmetic): the chip's rate for a launch of that size.  Successive
+    # launches read successive windows of a 4 GiB buffer, so none is served
+    # by the caches.
+    region = torch.empty(1 << 30, dtype=torch.int32, device=dev)
+    sp_sink = torch.empty(kvs.kvs_stream_probe_sink_words(), dtype=torch.int32, device=dev)
+
+    def stream_us(nbytes: int, reps: int = 12) -> float:
+        nbytes = min((int(nbytes) + 15) // 16 * 16, region.numel() * 4 // 2)
+        wins = region.numel() * 4 // nbytes
+        marks = []
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(int(cycles_per_ms * 2.0))
+            for i in range(reps):
+                win = region.view(torch.uint8)[(i % wins) * nbytes:]
+                a, b_ = ev(), ev()
+                a.record(stream)
+                kvs.kvs_stream_probe(win, nbytes, sp_sink, stream)
+                b_.record(stream)
+                marks.append((a, b_))
+        stream.synchronize()
+        return statistics.mean(a.elapsed_time(b_) for a, b_ in marks[2:]) * 1e3
+    plain = {"decode": statistics.mean(a["decode_launch"] for a in ab)}
+    if c.topk:
+        plain["score"] = statistics.mean(a["score_launch"] for a in ab)
+    plain_rows = {}
+    for k, nb in plain.items():
+        us = stream_us(nb)
+        plain_rows[f"plain_read_{k}_bytes"] = {
+            "us": round(us, 2), "bytes": int(nb), "GBps": round(nb / (us * 1e-6) / 1e9, 1),
+            "frac": round(nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "note": f"a plain contiguous read of the {k} launch's byte count (kvs_stream_probe)"}
+    del region
     t_plan = time.perf_counter()
     for _ in range(20):
         kvs.kvs_plan_split(wl.budgets, step.head_slot, c.Hp, 0.0, step.T)
@@ -833,6 +866,7 @@ def main() -> int:
                                          "bytes are the scoring's")
     rows["a4_plan"] = {"us_host": round(plan_us, 1), "note": f"S[{c.L}][{c.G}], host, ahead of time"}
     rows["a5_a6_decode_combine"] = row(kern["decode_attn"], "decode_launch")
+    rows.update(plain_rows)
     rows["gather_probe"] = {"us": round(pr_ms * 1e3, 2), "bytes": int(pr_bytes),
                             "GBps": round(pr_gbps, 1), "frac": round(pr_gbps / HBM_PEAK_GBPS, 4),
                             "note": "the decode's K/V tiles read through the page table, no "
@@ -881,6 +915,7 @@ def main() -> int:
             "traffic": traffic,
             "empirical_ceiling_GBps": round(pr_gbps, 1),
             "frac_of_empirical_ceiling": round(achieved / pr_gbps, 4),
+            "plain_read_same_bytes_GBps": plain_rows["plain_read_decode_bytes"]["GBps"],
         },
         "wall_ms_per_step_incl_flush": round(wall_ms / args.steps, 4),
         "step_ms_p10_p50_p90": [round(pct(0.1), 4), round(statistics.median(per_step), 4),

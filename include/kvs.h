@@ -447,6 +447,25 @@ int kvs_gather_probe(const kvs_paged_kv* cache, const int32_t* sel, const int32_
 int kvs_gather_probe_sink_words(int32_t d, int32_t* words);
 
 /*
+ * Plain read probe, a measurement aid (the chip's read rate for one launch
+ * of a given size, with no gather): reads the `bytes` contiguous bytes at
+ * src with the non-temporal 16-byte loads the kernels use, each wave of a
+ * resident grid an even contiguous share, and writes the XOR of the 32-bit
+ * words each wave read to one sink word per wave (sink words past the grid's
+ * waves are untouched); the XOR over the sink words is the XOR of every word
+ * read.
+ *   src         device, 16-byte aligned; bytes a positive multiple of 16
+ *               (KVS_EINVAL otherwise).
+ *   sink        device, sink_words >= kvs_stream_probe_sink_words (KVS_ENOSPC
+ *               otherwise).
+ */
+int kvs_stream_probe(const void* src, size_t bytes, uint32_t* sink, size_t sink_words,
+                     void* stream);
+
+/* Sink words kvs_stream_probe needs on the current device. */
+int kvs_stream_probe_sink_words(int32_t* words);
+
+/*
  * KV-cache codec [C 3, 7]: one chunk of T tokens of every layer,
  *     x[L][2][T][C] fp16 (index 1: 0 = K, 1 = V; C = all KV heads' channels
  *     of a token side by side),

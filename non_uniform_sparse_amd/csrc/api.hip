@@ -288,6 +288,27 @@ extern "C" int kvs_gather_probe(const kvs_paged_kv* cache, const int32_t* sel,
   return KVS_OK;
 }
 
+extern "C" int kvs_stream_probe_sink_words(int32_t* words) {
+  clear_error();
+  if (!words) return set_error(KVS_EINVAL, "kvs_stream_probe_sink_words: null output");
+  if (stream_probe_sink_words(words))
+    return set_error(KVS_EHIP, "kvs_stream_probe_sink_words: occupancy query failed");
+  return KVS_OK;
+}
+
+extern "C" int kvs_stream_probe(const void* src, size_t bytes, uint32_t* sink, size_t sink_words,
+                                void* stream) {
+  clear_error();
+  static const char* fn = "kvs_stream_probe";
+  if (!src || !sink) return set_error(KVS_EINVAL, "%s: null src or sink", fn);
+  if (!aligned16(src) || (bytes & 15) || bytes == 0)
+    return set_error(KVS_EINVAL, "%s: src 16-byte aligned, bytes a positive multiple of 16", fn);
+  if (hipError_t e = launch_stream_probe(src, bytes, sink, sink_words, (hipStream_t)stream))
+    return e == hipErrorInvalidValue ? set_error(KVS_ENOSPC, "%s: sink too small", fn)
+                                     : hip_error(e, fn);
+  return KVS_OK;
+}
+
 extern "C" int kvs_codec_decode(const kvs_codec_layout* layout, const kvs_codec_chunk* chunk,
                                 void* out, void* stream) {
   clear_error();

@@ -39,6 +39,9 @@ size_t prefill_workspace_bytes(int b, int Hkv, int C);
 hipError_t launch_probe(const CacheView& c, const int32_t* sel, const int32_t* sel_count, int K,
                         uint32_t* sink, size_t sink_words, hipStream_t s);
 int probe_sink_words(int d, int* words);
+hipError_t launch_stream_probe(const void* src, size_t bytes, uint32_t* sink, size_t sink_words,
+                               hipStream_t s);
+int stream_probe_sink_words(int* words);
 hipError_t launch_offload(const CacheView& c, const HostTierView& t, hipStream_t s);
 hipError_t launch_promote(const CacheView& c, const HostTierView& t, const int32_t* sel,
                           const int32_t* sel_count, int K, const HeadMask& heads, int32_t* moved,

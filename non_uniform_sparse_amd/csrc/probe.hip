@@ -13,6 +13,10 @@
 // (non-temporal), and the next unit's loads are issued before the current
 // one is folded; no load reaches past a batch's last unit.  A missing (null)
 // page loads page 0's tile, and those words are not folded.
+//
+// A second probe reads plain contiguous memory: the rate of a launch of a
+// given size with no gather at all, for comparing a kernel with a stream of
+// its own byte count.
 #include "flat_pages.h"
 #include "kvs_launch.h"
 
@@ -115,7 +119,63 @@ hipError_t launch_d(const CacheView& c, const int32_t* sel, const int32_t* sel_c
   return hipGetLastError();
 }
 
+// Plain read of n16 16-byte words: wave w of W reads words [n16 w/W,
+// n16 (w+1)/W), 64 lanes x CH non-temporal loads per step (CH KB per step),
+// two steps in flight, and folds them into one sink word.
+__global__ __launch_bounds__(kFlatThreads) void stream_probe_kernel(const uint4* __restrict__ src,
+                                                                    int64_t n16,
+                                                                    uint32_t* __restrict__ sink) {
+  constexpr int CH = 8;
+  const int lane = threadIdx.x & 63;
+  const int64_t W = (int64_t)gridDim.x * (kFlatThreads / 64);
+  const int64_t w = (int64_t)blockIdx.x * (kFlatThreads / 64) + (threadIdx.x >> 6);
+  const int64_t lo = n16 * w / W, hi = n16 * (w + 1) / W;
+  uint32_t acc = 0;
+  uint4 b0[CH], b1[CH];
+  auto load = [&](int64_t base, uint4 (&dst)[CH]) {
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int64_t i = base + 64 * k + lane;
+      dst[k] = i < hi ? ld16_once(src + i) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto fold = [&](const uint4 (&v)[CH]) {
+#pragma unroll
+    for (int k = 0; k < CH; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+  };
+  constexpr int64_t STEP = 64 * CH;
+  if (lo < hi) load(lo, b0);
+  for (int64_t base = lo; base < hi; base += 2 * STEP) {   // no load past hi (uniform tests)
+    if (base + STEP < hi) load(base + STEP, b1);
+    fold(b0);
+    if (base + 2 * STEP < hi) load(base + 2 * STEP, b0);
+    if (base + STEP < hi) fold(b1);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc ^= __shfl_xor(acc, off, 64);
+  if (lane == 0) sink[w] = acc;
+}
+
+const void* stream_probe_symbol() { return reinterpret_cast<const void*>(&stream_probe_kernel); }
+
 }  // namespace
+
+hipError_t launch_stream_probe(const void* src, size_t bytes, uint32_t* sink, size_t sink_words,
+                               hipStream_t s) {
+  int grid = 0;
+  if (hipError_t e = resident_grid<stream_probe_symbol>(&grid)) return e;
+  if ((size_t)grid * (kFlatThreads / 64) > sink_words) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(stream_probe_kernel, dim3((unsigned)grid), dim3(kFlatThreads), 0, s,
+                     static_cast<const uint4*>(src), (int64_t)(bytes / 16), sink);
+  return hipGetLastError();
+}
+
+int stream_probe_sink_words(int* words) {
+  int grid = 0;
+  if (resident_grid<stream_probe_symbol>(&grid)) return -1;
+  *words = grid * (kFlatThreads / 64);
+  return 0;
+}
 
 hipError_t launch_probe(const CacheView& c, const int32_t* sel, const int32_t* sel_count, int K,
                         uint32_t* sink, size_t sink_words, hipStream_t s) {

@@ -30,7 +30,8 @@ EXPORTS = (
     "kvs_prefill_workspace_bytes",
     "kvs_offload_pages", "kvs_promote_pages", "kvs_append_kv_tier",
     "kvs_codec_bounds", "kvs_codec_encode", "kvs_codec_decode",
-    "kvs_gather_probe", "kvs_gather_probe_sink_words",
+    "kvs_gather_probe", "kvs_gather_probe_sink_words", "kvs_stream_probe",
+    "kvs_stream_probe_sink_words",
     "kvs_plan_split",
     "kvs_decode_attn", "kvs_decode_attn_noalloc",
     "kvs_decode_workspace_bytes", "kvs_decode_concurrency", "kvs_cluster_heads",
@@ -129,6 +130,8 @@ def lib() -> ctypes.CDLL:
         L.kvs_codec_decode.argtypes = [play, pch, vp, vp]
         L.kvs_gather_probe.argtypes = [pkv, vp, vp, i32, vp, ctypes.c_size_t, vp]
         L.kvs_gather_probe_sink_words.argtypes = [i32, ctypes.POINTER(i32)]
+        L.kvs_stream_probe.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_size_t, vp]
+        L.kvs_stream_probe_sink_words.argtypes = [ctypes.POINTER(i32)]
         L.kvs_plan_split.argtypes = [vp, vp, i32, i32, i32, f64, i32, vp]
         L.kvs_decode_attn.argtypes = [pkv, vp, vp, vp, i32, vp, f32, vp, ctypes.c_size_t, vp, vp]
         L.kvs_decode_attn_noalloc.argtypes = [pkv, vp, vp, vp, i32, vp, f32, vp, vp]
@@ -444,6 +447,21 @@ def kvs_gather_probe(cache: Cache, sel: Optional[torch.Tensor], sel_count: Optio
         raise ValueError("sink: contiguous int32 on the cache's device")
     _check(lib().kvs_gather_probe(ctypes.byref(s), _ptr(sel), _ptr(sel_count), K, _ptr(sink),
                                   sink.numel(), _stream(stream)))
+
+
+def kvs_stream_probe_sink_words() -> int:
+    w = ctypes.c_int32(0)
+    _check(lib().kvs_stream_probe_sink_words(ctypes.byref(w)))
+    return w.value
+
+
+def kvs_stream_probe(src: torch.Tensor, nbytes: int, sink: torch.Tensor, stream=None) -> None:
+    """Plain read of the first ``nbytes`` bytes of ``src`` (a contiguous device
+    tensor); one XOR word per wave into ``sink`` (int32)."""
+    if not src.is_contiguous() or nbytes > src.numel() * src.element_size():
+        raise ValueError("src must be contiguous and hold nbytes")
+    _check(lib().kvs_stream_probe(_ptr(src), int(nbytes), _ptr(sink), sink.numel(),
+                                  _stream(stream)))
 
 
 def kvs_prefill_workspace_bytes(b: int, Hkv: int, C: int) -> int:

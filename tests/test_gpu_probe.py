@@ -66,3 +66,25 @@ def test_gather_probe_reads_the_attended_tiles(name, ov, null_pages):
                  None if cnt is None else cnt.cpu().numpy(), c.P)
     assert got == want
     assert np.all(sink[-7:].cpu().numpy() == 0)                # words past the grid untouched
+
+
+@pytest.mark.parametrize("nbytes", [16, 16 * 1000, 16 * 64 * 8 * 2 + 48, 48 << 20])
+def test_stream_probe_reads_exactly_the_range(nbytes):
+    """The plain-read probe folds every word of the first nbytes and nothing
+    past them: the XOR over its sink equals the XOR of those words, and a
+    poisoned tail beyond nbytes leaves it unchanged."""
+    require_gpu()
+    say(f"[case] stream probe {nbytes} bytes")
+    g = torch.Generator(device="cpu").manual_seed(3)
+    words = torch.randint(-2**31, 2**31 - 1, (nbytes // 4 + 1024,), generator=g, dtype=torch.int32)
+    src = words.to("cuda")
+    sink = torch.zeros(kvs.kvs_stream_probe_sink_words(), dtype=torch.int32, device="cuda")
+    kvs.kvs_stream_probe(src, nbytes, sink)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    want = np.bitwise_xor.reduce(words[: nbytes // 4].numpy().view(np.uint32))
+    assert got == want
+    with pytest.raises(kvs.KvsError):
+        kvs.kvs_stream_probe(src, nbytes + 8, sink)        # not a multiple of 16
+    with pytest.raises(kvs.KvsError):
+        kvs.kvs_stream_probe(src, nbytes, sink[:1])        # sink too small
