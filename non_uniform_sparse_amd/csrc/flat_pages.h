@@ -83,11 +83,11 @@ struct FlatShare {
 
 __device__ __forceinline__ FlatShare flat_share(const int* pre, int BH) {
   const int64_t W = (int64_t)gridDim.x * (kFlatThreads / 64);
-  const int64_t w = (int64_t)blockIdx.x * (kFlatThreads / 64) + (threadIdx.x >> 6);
+  const int64_t w = (int64_t)blockIdx.x * (kFlatThreads / 64) + uni(threadIdx.x >> 6);
   const int64_t T = uni(pre[BH]);
   FlatShare s;
-  s.t0 = (int)(T * w / W);
-  s.t1 = (int)(T * (w + 1) / W);
+  s.t0 = uni((int)(T * w / W));
+  s.t1 = uni((int)(T * (w + 1) / W));
   int lo = 0, hi = BH;
   while (lo < hi) {
     const int mid = (lo + hi + 1) / 2;
