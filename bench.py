@@ -73,6 +73,10 @@ def algorithmic_bytes(step: DecodeStep, l: int) -> dict:
     maxpg = step.layouts[l].page_table.shape[2]
     return {"kv": kv, "meta": meta, "small": small, "tokens": toks, "units": units,
             "decode_launch": kv + rows * (c.d + 1) * 4 * 2 + c.b * c.Hq * c.d * (s + 4),
+            # its two kernels: the split-K decode (KV and q read, partials
+            # written) and the combine (partials read, output written)
+            "splits_launch": kv + rows * (c.d + 1) * 4 + c.b * c.Hq * c.d * s,
+            "combine_launch": rows * (c.d + 1) * 4 + c.b * c.Hq * c.d * 4,
             # per-call bytes of the other rows
             "score_launch": meta + c.b * c.Hq * c.d * s + c.b * c.Hkv * maxpg * 4,
             "topk_launch": int(npg.sum()) * 4 + c.b * c.Hkv * (c.topk or 0) * 4 + c.b * c.Hkv * 4,
@@ -80,9 +84,10 @@ def algorithmic_bytes(step: DecodeStep, l: int) -> dict:
 
 
 def stored_traffic(workload: str):
-    """HBM bytes per kvs_decode_attn launch from the committed rocprofv3 PMC
-    record of this workload (FETCH_SIZE and WRITE_SIZE, scaled by a copy of
-    known size), or None if there is none or the decode source changed since."""
+    """HBM bytes per split-K decode kernel launch from the committed
+    rocprofv3 PMC record of this workload (FETCH_SIZE and WRITE_SIZE, scaled
+    by a copy of known size), or None if there is none or the decode source
+    changed since."""
     from non_uniform_sparse_amd import profiling
     path = os.path.join(ROOT, "profiles", f"decode_traffic_{workload}.json")
     if not os.path.exists(path):
@@ -713,7 +718,8 @@ def main() -> int:
     # spin long enough for the host to enqueue the whole step, so the
     # kernels run back to back and the events time kernels, not host
     # launch latency.
-    kern = {"score": [], "topk": [], "select": [], "decode_attn": []}
+    kern = {"score": [], "topk": [], "select": [], "decode_splits": [], "decode_combine": [],
+            "decode_attn": []}
     for _ in range(args.steps):
         with torch.cuda.stream(stream):
             torch.cuda._sleep(int(cycles_per_ms * (2.0 + 0.4 * c.L)))
@@ -744,6 +750,29 @@ def main() -> int:
             step.attend(l, q, stream)
             e1.record(stream)
             marks.append(("decode_attn", e0, e1))
+        stream.synchronize()
+        for k, a, b_ in marks:
+            kern[k].append(a.elapsed_time(b_))
+        # the decode's two kernels again, as the two calls kvs_decode_splits
+        # and kvs_decode_combine (the same kernels as one kvs_decode_attn),
+        # each timed alone
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(int(cycles_per_ms * (1.0 + 0.2 * c.L)))
+            if flush is not None:
+                flush.sum()
+        marks = []
+        for l in range(c.L):
+            buf = step.bufs[l]
+            dargs = (step.caches[l], qs[l], buf.sel, buf.sel_count, c.topk or 0, step.S[l],
+                     step.scale, step.workspace, buf.out, stream)
+            e0, e1, e2 = ev(), ev(), ev()
+            e0.record(stream)
+            kvs.kvs_decode_splits(*dargs)
+            e1.record(stream)
+            kvs.kvs_decode_combine(*dargs)
+            e2.record(stream)
+            marks.append(("decode_splits", e0, e1))
+            marks.append(("decode_combine", e1, e2))
         stream.synchronize()
         for k, a, b_ in marks:
             kern[k].append(a.elapsed_time(b_))
@@ -833,7 +862,7 @@ def main() -> int:
                 marks.append((a, b_))
         stream.synchronize()
         return statistics.mean(a.elapsed_time(b_) for a, b_ in marks[2:]) * 1e3
-    plain = {"decode": statistics.mean(a["decode_launch"] for a in ab)}
+    plain = {"decode": statistics.mean(a["splits_launch"] for a in ab)}
     if c.topk:
         plain["score"] = statistics.mean(a["score_launch"] for a in ab)
     plain_rows = {}
@@ -865,15 +894,22 @@ def main() -> int:
                                     note="scores and top-K in one launch (kvs_select_pages); "
                                          "bytes are the scoring's")
     rows["a4_plan"] = {"us_host": round(plan_us, 1), "note": f"S[{c.L}][{c.G}], host, ahead of time"}
-    rows["a5_a6_decode_combine"] = row(kern["decode_attn"], "decode_launch")
+    rows["a5_decode_splits"] = dict(row(kern["decode_splits"], "splits_launch"),
+                                    note="the split-K decode kernel alone (kvs_decode_splits)")
+    rows["a6_combine"] = dict(row(kern["decode_combine"], "combine_launch"),
+                              note="the LSE combine kernel alone (kvs_decode_combine)")
+    rows["a5_a6_decode_combine"] = dict(row(kern["decode_attn"], "decode_launch"),
+                                        note="one kvs_decode_attn call: both kernels and the "
+                                             "gap between them")
     rows.update(plain_rows)
     rows["gather_probe"] = {"us": round(pr_ms * 1e3, 2), "bytes": int(pr_bytes),
                             "GBps": round(pr_gbps, 1), "frac": round(pr_gbps / HBM_PEAK_GBPS, 4),
                             "note": "the decode's K/V tiles read through the page table, no "
                                     "arithmetic: the access pattern's empirical ceiling"}
     pct = lambda f: per_step[min(len(per_step) - 1, int(f * len(per_step)))]
-    dec_ms = statistics.mean(kern["decode_attn"])
-    dec_bytes = statistics.mean(a["decode_launch"] for a in ab)
+    # The dominant kernel: the split-K decode, timed alone.
+    dec_ms = statistics.mean(kern["decode_splits"])
+    dec_bytes = statistics.mean(a["splits_launch"] for a in ab)
     achieved = dec_bytes / (dec_ms * 1e-3) / 1e9
     value = kv_bytes / (ms * 1e-3) / 1e9
     traffic = stored_traffic(c.name)
@@ -907,7 +943,7 @@ def main() -> int:
         "rows": rows,
         "roofline": {
             "bound": "hbm",
-            "kernel": "kvs_decode_attn (split-K decode + combine)",
+            "kernel": "decode_kernel (the split-K decode, kvs_decode_splits)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
@@ -916,6 +952,7 @@ def main() -> int:
             "empirical_ceiling_GBps": round(pr_gbps, 1),
             "frac_of_empirical_ceiling": round(achieved / pr_gbps, 4),
             "plain_read_same_bytes_GBps": plain_rows["plain_read_decode_bytes"]["GBps"],
+            "with_combine_frac": rows["a5_a6_decode_combine"]["frac"],
         },
         "wall_ms_per_step_incl_flush": round(wall_ms / args.steps, 4),
         "step_ms_p10_p50_p90": [round(pct(0.1), 4), round(statistics.median(per_step), 4),

@@ -391,6 +391,30 @@ int kvs_decode_attn(const kvs_paged_kv* cache, const void* q, const int32_t* sel
                     void* workspace, size_t ws_bytes, float* out, void* stream);
 
 /*
+ * The two phases of kvs_decode_attn as calls of their own: the ragged
+ * split-K decode [T 3.2, 3.3] and the log-sum-exp combine of the splits [F
+ * Core method].  Both take exactly kvs_decode_attn's arguments and make its
+ * checks; kvs_decode_splits launches only the split kernel, which writes
+ * every split's partial output and log-sum-exp (and each head's first and
+ * last split) into `workspace`; kvs_decode_combine launches only the
+ * combine, which reads them from `workspace` and writes `out`.  The two
+ * called in that order on one stream, with the same arguments and workspace
+ * (and nothing writing that workspace in between), give bit for bit the
+ * output of one kvs_decode_attn call.  kvs_decode_combine on a workspace no
+ * kvs_decode_splits call has filled for these arguments reads whatever the
+ * workspace holds (finite or not): the result is then undefined, though
+ * every access stays inside the workspace and `out`.  q and scale are
+ * checked but not used by kvs_decode_combine; out is not written by
+ * kvs_decode_splits.
+ */
+int kvs_decode_splits(const kvs_paged_kv* cache, const void* q, const int32_t* sel,
+                      const int32_t* sel_count, int32_t K, const int32_t* S_row, float scale,
+                      void* workspace, size_t ws_bytes, float* out, void* stream);
+int kvs_decode_combine(const kvs_paged_kv* cache, const void* q, const int32_t* sel,
+                       const int32_t* sel_count, int32_t K, const int32_t* S_row, float scale,
+                       void* workspace, size_t ws_bytes, float* out, void* stream);
+
+/*
  * kvs_decode_attn for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the same kernels and results, with the workspace taken from scratch memory

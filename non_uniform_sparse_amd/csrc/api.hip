@@ -485,9 +485,13 @@ int decode_prepare(const kvs_paged_kv* cache, const void* q, const int32_t* sel,
   return KVS_OK;
 }
 
+// Which kernels decode_launch runs.
+enum : int { kSplitPhase = 1, kCombinePhase = 2, kBothPhases = 3 };
+
 // Carves the workspace (256-byte aligned, large enough) and launches the
-// split kernel and the combine.
-int decode_launch(DecodeArgs& a, void* workspace, size_t stamps_at, hipStream_t s) {
+// split kernel, the combine, or both.
+int decode_launch(DecodeArgs& a, void* workspace, size_t stamps_at, hipStream_t s,
+                  int phases = kBothPhases) {
   char* ws = static_cast<char*>(workspace);
   const size_t rows = (size_t)a.c.b * a.c.Hq * a.Smax;
   a.o_part = reinterpret_cast<float*>(ws);
@@ -502,18 +506,20 @@ int decode_launch(DecodeArgs& a, void* workspace, size_t stamps_at, hipStream_t 
 #else
   (void)stamps_at;
 #endif
-  if (hipError_t e = launch_decode(a, s)) return hip_error(e, "kvs_decode_attn (split kernel)");
-  if (hipError_t e = launch_combine(a, s)) return hip_error(e, "kvs_decode_attn (combine kernel)");
+  if (phases & kSplitPhase)
+    if (hipError_t e = launch_decode(a, s)) return hip_error(e, "decode (split kernel)");
+  if (phases & kCombinePhase)
+    if (hipError_t e = launch_combine(a, s)) return hip_error(e, "decode (combine kernel)");
   return KVS_OK;
 }
-}  // namespace
 
-extern "C" int kvs_decode_attn(const kvs_paged_kv* cache, const void* q, const int32_t* sel,
-                               const int32_t* sel_count, int32_t K, const int32_t* S_row,
-                               float scale, void* workspace, size_t ws_bytes, float* out,
-                               void* stream) {
+// kvs_decode_attn, kvs_decode_splits and kvs_decode_combine: the same
+// checks, then the phases asked for.
+int decode_entry(const kvs_paged_kv* cache, const void* q, const int32_t* sel,
+                 const int32_t* sel_count, int32_t K, const int32_t* S_row, float scale,
+                 void* workspace, size_t ws_bytes, float* out, void* stream, const char* fn,
+                 int phases) {
   clear_error();
-  const char* fn = "kvs_decode_attn";
   DecodeArgs a;
   size_t need = 0, stamps_at = 0;
   if (int rc = decode_prepare(cache, q, sel, sel_count, K, S_row, scale, out, fn, &a, &need,
@@ -523,7 +529,32 @@ extern "C" int kvs_decode_attn(const kvs_paged_kv* cache, const void* q, const i
     return set_error(KVS_EINVAL, "%s: workspace must be non-null and 256-byte aligned", fn);
   if (ws_bytes < need)
     return set_error(KVS_ENOSPC, "%s: workspace %zu bytes < %zu needed", fn, ws_bytes, need);
-  return decode_launch(a, workspace, stamps_at, (hipStream_t)stream);
+  return decode_launch(a, workspace, stamps_at, (hipStream_t)stream, phases);
+}
+}  // namespace
+
+extern "C" int kvs_decode_attn(const kvs_paged_kv* cache, const void* q, const int32_t* sel,
+                               const int32_t* sel_count, int32_t K, const int32_t* S_row,
+                               float scale, void* workspace, size_t ws_bytes, float* out,
+                               void* stream) {
+  return decode_entry(cache, q, sel, sel_count, K, S_row, scale, workspace, ws_bytes, out, stream,
+                      "kvs_decode_attn", kBothPhases);
+}
+
+extern "C" int kvs_decode_splits(const kvs_paged_kv* cache, const void* q, const int32_t* sel,
+                                 const int32_t* sel_count, int32_t K, const int32_t* S_row,
+                                 float scale, void* workspace, size_t ws_bytes, float* out,
+                                 void* stream) {
+  return decode_entry(cache, q, sel, sel_count, K, S_row, scale, workspace, ws_bytes, out, stream,
+                      "kvs_decode_splits", kSplitPhase);
+}
+
+extern "C" int kvs_decode_combine(const kvs_paged_kv* cache, const void* q, const int32_t* sel,
+                                  const int32_t* sel_count, int32_t K, const int32_t* S_row,
+                                  float scale, void* workspace, size_t ws_bytes, float* out,
+                                  void* stream) {
+  return decode_entry(cache, q, sel, sel_count, K, S_row, scale, workspace, ws_bytes, out, stream,
+                      "kvs_decode_combine", kCombinePhase);
 }
 
 // ---------------------------------------------------------------------------
@@ -601,6 +632,20 @@ extern "C" int kvs_decode_concurrency(int32_t device, int32_t d, int32_t gqa, in
 }
 
 #ifdef KVS_WG_STAMPS
+namespace kvs {
+hipError_t copy_score_stamps(uint64_t* dst, size_t waves, hipStream_t s);
+}
+// Instrumented build only: the [waves][3] uint64 clock stamps (entry, share
+// known, exit) of the last scoring launch's first `waves` waves, copied to
+// dst (device) on `stream`.
+extern "C" int kvs_score_stamps(uint64_t* dst, size_t waves, void* stream) {
+  clear_error();
+  if (!dst) return set_error(KVS_EINVAL, "kvs_score_stamps: null dst");
+  if (hipError_t e = copy_score_stamps(dst, waves, (hipStream_t)stream))
+    return hip_error(e, "kvs_score_stamps");
+  return KVS_OK;
+}
+
 // Instrumented build only: byte offset of the [b * sum(S_row)][2] uint64
 // start/end stamps (s_memrealtime, 100 MHz) inside the decode workspace.
 extern "C" size_t kvs_decode_stamps_offset(int32_t b, int32_t Hq, int32_t Hkv, int32_t d,

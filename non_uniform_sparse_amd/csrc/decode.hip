@@ -187,23 +187,31 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   if (cur_j >= 0) end_head(cur_j);
 }
 
-// One workgroup of W = blockDim.x / 64 waves (1 to 4) per (request, query
+// Waves per combine workgroup at most: 16 at d = 128; 8 at d = 256, whose
+// rows need twice the registers.
+template <int D>
+constexpr int kCombineWaves = D == 128 ? 16 : 8;
+
+// One workgroup of W = blockDim.x / 64 waves (1 to 16) per (request, query
 // head).  The splits that touched the head form the contiguous range
 // [first, last] that the decode kernel recorded (an empty split inside it
-// carries lse = -inf).  Every wave forms M = max lse over the whole range
-// (lane = split), then merges its own W-th of the range, 8 splits per step:
-// lane l takes split l / 8 of the step (its weight 2^(lse - M) comes by
-// shuffle) and channels (l % 8) * D/8 .. +D/8; the 8 split lanes of each
-// channel chunk are summed with DPP / lane swaps.  The waves' sums meet in
-// LDS and are added in wave order, so the result does not depend on timing.
-// A head spanning hundreds of splits (long, full-budget heads) is thus not
-// one wave's serial walk.
+// carries lse = -inf).  Wave w merges its W-th of the range, 8 splits per
+// step: lane l takes split l / 8 of the step and channels (l % 8) * D/8 ..
+// +D/8, and the wave keeps a running maximum m of the lse it has seen, its
+// weighted sum and its total weight relative to m (a step that raises m
+// rescales both first).  The loads of the next step are in flight while a
+// step is merged, and no pass over the range precedes the merge.  The 8
+// split lanes of each channel chunk are summed with DPP / lane swaps; the
+// waves' (m, sum, weight) meet in LDS and are merged in wave order, so the
+// result does not depend on timing.  A head spanning hundreds of splits
+// (long, full-budget heads) is thus spread over up to 16 waves.
 template <int D>
-__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kCombineWaves<D>) void combine_kernel(DecodeArgs a) {
   constexpr int CH = D / 8;          // channels per lane
   constexpr int V4 = CH / 4;         // float4 loads per split row
-  __shared__ float s_acc[4][D];
-  __shared__ float s_den[4];
+  constexpr int kMaxWaves = kCombineWaves<D>;
+  __shared__ float s_acc[kMaxWaves][D];
+  __shared__ float s_m[kMaxWaves], s_den[kMaxWaves];
   const CacheView& c = a.c;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int W = blockDim.x >> 6;
@@ -220,51 +228,61 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
   const int s_lo = cnt > 0 ? clampi(lo, 0, a.Smax - 1) : 0;
   const int s_hi = cnt > 0 ? clampi(hi, s_lo, a.Smax - 1) : -1;
   const int64_t row = ((int64_t)r * c.Hq + g) * a.Smax;
-
-  float M = -__builtin_inff();
-  for (int w0 = s_lo; w0 <= s_hi; w0 += 64) {
-    const float v = w0 + lane <= s_hi ? a.lse_part[row + w0 + lane] : -__builtin_inff();
-    M = fmaxf(M, v);
-  }
-  M = group_max<64>(M);
   // this wave's part of the range
   const int per = (s_hi - s_lo + 1 + W - 1) / W;
   const int w_lo = s_lo + wave * per, w_hi = min(s_hi, w_lo + per - 1);
+  const int sl = lane / 8, dc = lane % 8;
+
   float acc[CH];
 #pragma unroll
   for (int e = 0; e < CH; ++e) acc[e] = 0.f;
-  float den = 0.f;
-  const int sl = lane / 8, dc = lane % 8;
-  if (M > -__builtin_inff()) {
-    for (int w0 = w_lo; w0 <= w_hi; w0 += 64) {
-      const float lw = w0 + lane <= w_hi ? a.lse_part[row + w0 + lane] : -__builtin_inff();
-      const float wt = __builtin_amdgcn_exp2f(lw - M);   // 0 for an empty split
-      den += wt;
-      const int nsp = min(64, w_hi - w0 + 1);
-      for (int s8 = 0; s8 < nsp; s8 += 8) {
-        const int sp = s8 + sl;
-        const float w = __shfl(wt, sp, 64);
-        const bool ok = sp < nsp && w > 0.f;
-        // in-bounds row even when unused; an unused row may hold stale data,
-        // so its contribution is selected away, never multiplied in
-        const float4* src =
-            reinterpret_cast<const float4*>(a.o_part + (row + w0 + min(sp, nsp - 1)) * D + dc * CH);
+  float m = -__builtin_inff(), den = 0.f;
+  // One step: the lse of split s0 + sl and its row slice (an in-bounds row
+  // even past w_hi; such a lane's lse is -inf and its row is never used).
+  auto load = [&](int s0, float& lse, float4 (&x)[V4]) {
+    const int sp = s0 + sl;
+    lse = sp <= w_hi ? a.lse_part[row + sp] : -__builtin_inff();
+    const float4* src =
+        reinterpret_cast<const float4*>(a.o_part + (row + min(sp, w_hi)) * D + dc * CH);
 #pragma unroll
-        for (int v = 0; v < V4; ++v) {
-          const float4 x = src[v];
-          acc[4 * v] += ok ? w * x.x : 0.f;
-          acc[4 * v + 1] += ok ? w * x.y : 0.f;
-          acc[4 * v + 2] += ok ? w * x.z : 0.f;
-          acc[4 * v + 3] += ok ? w * x.w : 0.f;
-        }
-      }
+    for (int v = 0; v < V4; ++v) x[v] = src[v];
+  };
+  auto merge = [&](float lse, const float4 (&x)[V4]) {
+    const float m_new = fmaxf(m, group_max<64>(lse));   // uniform over the wave
+    if (!(m_new > -__builtin_inff())) return;           // nothing valid yet
+    const float keep = m > -__builtin_inff() ? __builtin_amdgcn_exp2f(m - m_new) : 0.f;
+    // an empty split (lse = -inf) weighs 0; its row may hold stale data, so
+    // its contribution is selected away, never multiplied in
+    const float wt = lse > -__builtin_inff() ? __builtin_amdgcn_exp2f(lse - m_new) : 0.f;
+    const bool use = wt > 0.f;
+    den = den * keep + wt;
+#pragma unroll
+    for (int v = 0; v < V4; ++v) {
+      acc[4 * v] = acc[4 * v] * keep + (use ? wt * x[v].x : 0.f);
+      acc[4 * v + 1] = acc[4 * v + 1] * keep + (use ? wt * x[v].y : 0.f);
+      acc[4 * v + 2] = acc[4 * v + 2] * keep + (use ? wt * x[v].z : 0.f);
+      acc[4 * v + 3] = acc[4 * v + 3] * keep + (use ? wt * x[v].w : 0.f);
+    }
+    m = m_new;
+  };
+  if (w_lo <= w_hi) {
+    float l0, l1;
+    float4 x0[V4], x1[V4];
+    load(w_lo, l0, x0);
+    for (int s0 = w_lo; s0 <= w_hi; s0 += 16) {   // no load past w_hi's step (uniform tests)
+      if (s0 + 8 <= w_hi) load(s0 + 8, l1, x1);
+      merge(l0, x0);
+      if (s0 + 16 <= w_hi) load(s0 + 16, l0, x0);
+      if (s0 + 8 <= w_hi) merge(l1, x1);
     }
   }
-  den = group_sum<64>(den);   // each split's weight is held by one lane
+  // sums over the 8 split lanes of each channel chunk (lanes dc + 8 sl)
+  den += dpp<0x128>(den);   // row_ror:8 -> lane ^ 8 within a row of 16
+  den = across_sum<16>(den);
 #pragma unroll
   for (int e = 0; e < CH; ++e) {
     float v = acc[e];
-    v += dpp<0x128>(v);   // row_ror:8 -> lane ^ 8 within a row of 16
+    v += dpp<0x128>(v);
     v = across_sum<16>(v);
     acc[e] = v;
   }
@@ -283,20 +301,29 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < CH; ++e) s_acc[wave][dc * CH + e] = acc[e];
   }
-  if (lane == 0) s_den[wave] = den;
+  if (lane == 0) {
+    s_m[wave] = m;
+    s_den[wave] = den;
+  }
   __syncthreads();
-  // wave 0 adds the waves' sums in wave order, D / 64 channels per lane
+  // wave 0 merges the waves' sums in wave order, D / 64 channels per lane
   if (wave == 0) {
-    float dsum = 0.f;
-    for (int w = 0; w < W; ++w) dsum += s_den[w];
+    float M = -__builtin_inff();
+    for (int w = 0; w < W; ++w) M = fmaxf(M, s_m[w]);
+    float dsum = 0.f, x[D / 64];
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) x[k] = 0.f;
+    if (M > -__builtin_inff()) {
+      for (int w = 0; w < W; ++w) {
+        const float sc = s_m[w] > -__builtin_inff() ? __builtin_amdgcn_exp2f(s_m[w] - M) : 0.f;
+        dsum += sc * s_den[w];
+#pragma unroll
+        for (int k = 0; k < D / 64; ++k) x[k] += sc * s_acc[w][lane + 64 * k];
+      }
+    }
     const float inv = dsum > 0.f ? 1.f / dsum : 0.f;
 #pragma unroll
-    for (int k = 0; k < D / 64; ++k) {
-      const int ch = lane + 64 * k;
-      float x = 0.f;
-      for (int w = 0; w < W; ++w) x += s_acc[w][ch];
-      dst[ch] = x * inv;
-    }
+    for (int k = 0; k < D / 64; ++k) dst[lane + 64 * k] = x[k] * inv;
   }
 }
 
@@ -342,9 +369,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t s) {
   const int64_t blocks = (int64_t)a.c.b * a.c.Hq;
-  // one wave per 128 splits a head can span (a group's splits, plus one on
-  // either side), at most 4
-  const int waves = std::min(4, std::max(1, (a.Smax + 2 + 127) / 128));
+  // one wave per 24 splits a head can span (a group's splits), at most
+  // kCombineWaves
+  const int per = (a.Smax + 23) / 24;
+  const int waves = std::max(1, std::min(a.c.d == 128 ? kCombineWaves<128> : kCombineWaves<256>, per));
   if (a.c.d == 128)
     hipLaunchKernelGGL((combine_kernel<128>), dim3((unsigned)blocks), dim3(64 * waves), 0, s, a);
   else

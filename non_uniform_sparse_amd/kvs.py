@@ -33,7 +33,7 @@ EXPORTS = (
     "kvs_gather_probe", "kvs_gather_probe_sink_words", "kvs_stream_probe",
     "kvs_stream_probe_sink_words",
     "kvs_plan_split",
-    "kvs_decode_attn", "kvs_decode_attn_noalloc",
+    "kvs_decode_attn", "kvs_decode_splits", "kvs_decode_combine", "kvs_decode_attn_noalloc",
     "kvs_decode_workspace_bytes", "kvs_decode_concurrency", "kvs_cluster_heads",
     "kvs_last_error",
 )
@@ -133,7 +133,8 @@ def lib() -> ctypes.CDLL:
         L.kvs_stream_probe.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_size_t, vp]
         L.kvs_stream_probe_sink_words.argtypes = [ctypes.POINTER(i32)]
         L.kvs_plan_split.argtypes = [vp, vp, i32, i32, i32, f64, i32, vp]
-        L.kvs_decode_attn.argtypes = [pkv, vp, vp, vp, i32, vp, f32, vp, ctypes.c_size_t, vp, vp]
+        for name in ("kvs_decode_attn", "kvs_decode_splits", "kvs_decode_combine"):
+            getattr(L, name).argtypes = [pkv, vp, vp, vp, i32, vp, f32, vp, ctypes.c_size_t, vp, vp]
         L.kvs_decode_attn_noalloc.argtypes = [pkv, vp, vp, vp, i32, vp, f32, vp, vp]
         L.kvs_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, vp, i32]
         L.kvs_decode_workspace_bytes.restype = ctypes.c_size_t
@@ -143,6 +144,8 @@ def lib() -> ctypes.CDLL:
         if hasattr(L, "kvs_decode_stamps_offset"):   # instrumented build only
             L.kvs_decode_stamps_offset.argtypes = [i32, i32, i32, i32, vp, i32]
             L.kvs_decode_stamps_offset.restype = ctypes.c_size_t
+            L.kvs_score_stamps.argtypes = [vp, ctypes.c_size_t, vp]
+            L.kvs_score_stamps.restype = ctypes.c_int
         for name in EXPORTS:
             if name not in ("kvs_decode_workspace_bytes", "kvs_prefill_workspace_bytes",
                             "kvs_last_error"):
@@ -511,9 +514,9 @@ def kvs_decode_workspace_bytes(b: int, Hq: int, Hkv: int, d: int, S_row: Sequenc
     return int(lib().kvs_decode_workspace_bytes(b, Hq, Hkv, d, S.ctypes.data, len(S)))
 
 
-def kvs_decode_attn(cache: Cache, q: torch.Tensor, sel: Optional[torch.Tensor],
-                    sel_count: Optional[torch.Tensor], K: int, S_row: Sequence[int], scale: float,
-                    workspace: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+def _decode_call(name: str, cache: Cache, q: torch.Tensor, sel: Optional[torch.Tensor],
+                 sel_count: Optional[torch.Tensor], K: int, S_row: Sequence[int], scale: float,
+                 workspace: torch.Tensor, out: torch.Tensor, stream) -> None:
     s = cache.struct()
     dev = cache.kv.device
     _need(q, "q", (s.b, s.Hq, s.d), cache.kv.dtype, dev)
@@ -527,9 +530,34 @@ def kvs_decode_attn(cache: Cache, q: torch.Tensor, sel: Optional[torch.Tensor],
     if S.shape != (s.Hkv // s.Hp,):
         raise ValueError(f"S_row must have one entry per group ({s.Hkv // s.Hp})")
     nbytes = workspace.numel() * workspace.element_size()
-    _check(lib().kvs_decode_attn(ctypes.byref(s), _ptr(q), _ptr(sel), _ptr(sel_count), int(K),
-                                 S.ctypes.data, float(scale), _ptr(workspace), nbytes, _ptr(out),
-                                 _stream(stream)))
+    _check(getattr(lib(), name)(ctypes.byref(s), _ptr(q), _ptr(sel), _ptr(sel_count), int(K),
+                                S.ctypes.data, float(scale), _ptr(workspace), nbytes, _ptr(out),
+                                _stream(stream)))
+
+
+def kvs_decode_attn(cache: Cache, q: torch.Tensor, sel: Optional[torch.Tensor],
+                    sel_count: Optional[torch.Tensor], K: int, S_row: Sequence[int], scale: float,
+                    workspace: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    _decode_call("kvs_decode_attn", cache, q, sel, sel_count, K, S_row, scale, workspace, out,
+                 stream)
+
+
+def kvs_decode_splits(cache: Cache, q: torch.Tensor, sel: Optional[torch.Tensor],
+                      sel_count: Optional[torch.Tensor], K: int, S_row: Sequence[int],
+                      scale: float, workspace: torch.Tensor, out: torch.Tensor,
+                      stream=None) -> None:
+    """The split-K phase of kvs_decode_attn alone (partials into workspace)."""
+    _decode_call("kvs_decode_splits", cache, q, sel, sel_count, K, S_row, scale, workspace, out,
+                 stream)
+
+
+def kvs_decode_combine(cache: Cache, q: torch.Tensor, sel: Optional[torch.Tensor],
+                       sel_count: Optional[torch.Tensor], K: int, S_row: Sequence[int],
+                       scale: float, workspace: torch.Tensor, out: torch.Tensor,
+                       stream=None) -> None:
+    """The combine phase of kvs_decode_attn alone (workspace partials into out)."""
+    _decode_call("kvs_decode_combine", cache, q, sel, sel_count, K, S_row, scale, workspace, out,
+                 stream)
 
 
 # Bytes of scratch the library holds per device for kvs_decode_attn_noalloc.
@@ -568,3 +596,8 @@ def kvs_decode_stamps_offset(b: int, Hq: int, Hkv: int, d: int, S_row: Sequence[
     S = np.ascontiguousarray(S_row, dtype=np.int32)
     return int(lib().kvs_decode_stamps_offset(b, Hq, Hkv, d, S.ctypes.data, len(S)))
 
+
+def kvs_score_stamps(dst: torch.Tensor, stream=None) -> None:
+    """Instrumented build only: clock stamps [waves][3] (entry, share known,
+    exit) of the last scoring launch into dst (int64 [waves][3])."""
+    _check(lib().kvs_score_stamps(_ptr(dst), dst.shape[0], _stream(stream)))

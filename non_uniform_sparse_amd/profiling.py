@@ -5,11 +5,11 @@
     python -m non_uniform_sparse_amd.profiling traffic --workload W --fetch DIR --write DIR \\
         --copy-fetch DIR --copy-write DIR --out FILE
 
-``traffic`` turns FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the decode
-kernels into bytes per kvs_decode_attn launch, each counter scaled by what
-it reads for a plain device copy of known size (1 GiB read + 1 GiB written),
-and tags the record with a hash of the decode source so stale records are
-ignored.
+``traffic`` turns FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the split-K
+decode kernel (and, alongside, the combine) into bytes per launch, each
+counter scaled by what it reads for a plain device copy of known size (1 GiB
+read + 1 GiB written), and tags the record with a hash of the decode source
+so stale records are ignored.
 """
 
 from __future__ import annotations
@@ -125,13 +125,17 @@ def write_traffic(workload, fetch, write, copy_fetch, copy_write, out, cmd) -> d
     cf = _counter(copy_fetch, "FETCH_SIZE", r"copy") * kib
     cw = _counter(copy_write, "WRITE_SIZE", r"copy") * kib
     fs, ws = COPY_BYTES / cf, COPY_BYTES / cw
-    f = _counter(fetch, "FETCH_SIZE", r"decode_kernel|combine_kernel") * kib * fs
-    w = _counter(write, "WRITE_SIZE", r"decode_kernel|combine_kernel") * kib * ws
-    rec = {"workload": workload, "kernel": "kvs_decode_attn (decode_kernel + combine_kernel)",
+    f = _counter(fetch, "FETCH_SIZE", r"decode_kernel") * kib * fs
+    w = _counter(write, "WRITE_SIZE", r"decode_kernel") * kib * ws
+    cf_ = _counter(fetch, "FETCH_SIZE", r"combine_kernel") * kib * fs
+    cw_ = _counter(write, "WRITE_SIZE", r"combine_kernel") * kib * ws
+    rec = {"workload": workload, "kernel": "decode_kernel (the split-K decode)",
            "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
            "fetch_bytes_per_launch": int(f), "write_bytes_per_launch": int(w),
-           "traffic_bytes_per_launch": int(f + w), "source_sha256": decode_source_hash(),
-           "commands": cmd}
+           "traffic_bytes_per_launch": int(f + w),
+           "combine_kernel": {"fetch_bytes_per_launch": int(cf_),
+                              "write_bytes_per_launch": int(cw_)},
+           "source_sha256": decode_source_hash(), "commands": cmd}
     json.dump(rec, open(out, "w"), indent=1)
     return rec
 

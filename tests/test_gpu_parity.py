@@ -110,6 +110,35 @@ def test_split_invariance(name):
         assert diff <= 1e-5
 
 
+@pytest.mark.parametrize("name", ["tiny_ragged", "flexicache_topk", "gemma3_mixed"])
+def test_phases_equal_one_call(name):
+    """kvs_decode_splits then kvs_decode_combine on the same workspace give
+    bit for bit what one kvs_decode_attn call gives (the same kernels); the
+    split phase alone leaves out untouched."""
+    wl, step = _full(name, **({"b": 6} if name == "flexicache_topk" else
+                              {"b": 8, "L": 2} if name == "gemma3_mixed" else {}))
+    c = wl.cfg
+    qs = step.queries()
+    for l in range(c.L):
+        if c.topk:
+            step.select(l, qs[l])
+        buf = step.bufs[l]
+        sel = buf.sel if c.topk else None
+        cnt = buf.sel_count if c.topk else None
+        one = step.attend(l, qs[l]).clone()
+        out = torch.full_like(one, float("nan"))
+        step.workspace.fill_(0xFF)            # NaN partials if a phase wrote nothing
+        args = (step.caches[l], qs[l], sel, cnt, c.topk or 0, step.S[l], step.scale,
+                step.workspace, out)
+        kvs.kvs_decode_splits(*args)
+        torch.cuda.synchronize()
+        assert torch.isnan(out).all(), "the split phase wrote out"
+        kvs.kvs_decode_combine(*args)
+        torch.cuda.synchronize()
+        assert torch.equal(out, one), f"{name} layer {l}: phases differ from one call"
+    say(f"{name}: split + combine calls equal kvs_decode_attn on {c.L} layer(s)")
+
+
 def test_full_topk_equals_dense():
     """With K at least every head's page count, top-K attention is dense
     attention over all retained tokens -- bit for bit, since the selected

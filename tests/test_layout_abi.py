@@ -171,8 +171,12 @@ def test_validation_before_launch(kw, code):
     assert L.kvs_score_pages(ctypes.byref(s), 0x60000, 0x70000, None) == code
 
 
-def test_decode_validation():
+@pytest.mark.parametrize("name", ["kvs_decode_attn", "kvs_decode_splits", "kvs_decode_combine"])
+def test_decode_validation(name):
+    """The decode and its two phases as separate calls make the same checks,
+    all before any HIP call."""
     L = _lib()
+    fn = getattr(L, name)
     s = _FakeCache().s
     S = np.array([2, 2], dtype=np.int32)
     need = kvs.kvs_decode_workspace_bytes(1, 32, 8, 128, S)
@@ -180,13 +184,14 @@ def test_decode_validation():
     args = lambda **k: [ctypes.byref(s), k.get("q", 0x60000), k.get("sel", None), k.get("cnt", None),
                         k.get("K", 0), k.get("S", S).ctypes.data, ctypes.c_float(k.get("scale", 0.088)),
                         k.get("ws", 0x100000), k.get("wsb", need), k.get("out", 0x80000), None]
-    assert L.kvs_decode_attn(*args(wsb=need - 1)) == kvs.KVS_ENOSPC
-    assert L.kvs_decode_attn(*args(S=np.array([2, 0], dtype=np.int32))) == kvs.KVS_EINVAL
-    assert L.kvs_decode_attn(*args(sel=0x90000, cnt=None, K=4)) == kvs.KVS_EINVAL
-    assert L.kvs_decode_attn(*args(sel=0x90000, cnt=0xA0000, K=0)) == kvs.KVS_EINVAL
-    assert L.kvs_decode_attn(*args(scale=-1.0)) == kvs.KVS_EINVAL
-    assert L.kvs_decode_attn(*args(ws=0x100010)) == kvs.KVS_EINVAL   # workspace alignment
-    assert L.kvs_decode_attn(*args(q=0)) == kvs.KVS_EINVAL
+    assert fn(*args(wsb=need - 1)) == kvs.KVS_ENOSPC
+    assert name in kvs.last_error()
+    assert fn(*args(S=np.array([2, 0], dtype=np.int32))) == kvs.KVS_EINVAL
+    assert fn(*args(sel=0x90000, cnt=None, K=4)) == kvs.KVS_EINVAL
+    assert fn(*args(sel=0x90000, cnt=0xA0000, K=0)) == kvs.KVS_EINVAL
+    assert fn(*args(scale=-1.0)) == kvs.KVS_EINVAL
+    assert fn(*args(ws=0x100010)) == kvs.KVS_EINVAL   # workspace alignment
+    assert fn(*args(q=0)) == kvs.KVS_EINVAL
 
 
 def test_decode_noalloc_validation():
