@@ -634,6 +634,18 @@ extern "C" int kvs_decode_concurrency(int32_t device, int32_t d, int32_t gqa, in
 #ifdef KVS_WG_STAMPS
 namespace kvs {
 hipError_t copy_score_stamps(uint64_t* dst, size_t waves, hipStream_t s);
+hipError_t copy_select_stamps(uint64_t* dst, size_t blocks, hipStream_t s);
+}
+// Instrumented build only: the [blocks][12] uint64 clock stamps (entry, each
+// of up to eight waves' scoring done, past the barrier, K-th key known,
+// exit) of the last one-launch selection's first `blocks` workgroups, copied
+// to dst (device).
+extern "C" int kvs_select_stamps(uint64_t* dst, size_t blocks, void* stream) {
+  clear_error();
+  if (!dst) return set_error(KVS_EINVAL, "kvs_select_stamps: null dst");
+  if (hipError_t e = copy_select_stamps(dst, blocks, (hipStream_t)stream))
+    return hip_error(e, "kvs_select_stamps");
+  return KVS_OK;
 }
 // Instrumented build only: the [waves][3] uint64 clock stamps (entry, share
 // known, exit) of the last scoring launch's first `waves` waves, copied to

@@ -22,7 +22,27 @@ constexpr int P = 16;
 // Rounds of bounds per wave: one scored, one in flight (deeper rings measured
 // slower here).
 constexpr int kRing = 2;
+
 constexpr int kRoundRegs = 32;   // 64 and 128 measured slower
+
+#ifdef KVS_WG_STAMPS
+// Instrumented build only: per workgroup of the last launch, the clock
+// (s_memrealtime, 100 MHz) at entry [0], when wave w has scored its pages
+// [1 + w], past the barrier after scoring [9], once the K-th key is known
+// [10], and at exit [11], each stored when taken.
+constexpr int kSelectStampBlocks = 16384;
+constexpr int kSelectStamps = 12;
+__device__ uint64_t g_select_stamps[kSelectStampBlocks][kSelectStamps];
+#define KVS_SELECT_STAMP(k)                                                         \
+  do {                                                                              \
+    if (blockIdx.x < kSelectStampBlocks)                                            \
+      g_select_stamps[blockIdx.x][k] = __builtin_amdgcn_s_memrealtime();            \
+  } while (0)
+#else
+#define KVS_SELECT_STAMP(k) \
+  do {                      \
+  } while (0)
+#endif
 
 template <int D, int GQ, typename DT>
 __global__ __launch_bounds__(kSelThreads) void select_pages_kernel(
@@ -34,6 +54,7 @@ __global__ __launch_bounds__(kSelThreads) void select_pages_kernel(
   const int r = rh / c.Hkv, h = rh - r * c.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int ql = lane % 8;
+  if (tid == 0) KVS_SELECT_STAMP(0);
   const int npg = (clampi(c.seq_len[rh], 0, P * c.maxpg) + P - 1) / P;
   const int keep = min(K, npg);
   const int hs = c.head_slot[h];
@@ -57,13 +78,17 @@ __global__ __launch_bounds__(kSelThreads) void select_pages_kernel(
   }
   if (srow)
     for (int p = npg + tid; p < c.maxpg; p += kSelThreads) srow[p] = -__builtin_inff();
+  if (lane == 0) KVS_SELECT_STAMP(1 + wid);
   __syncthreads();
+  if (tid == 0) KVS_SELECT_STAMP(9);
 
   int32_t* out = sel + (int64_t)rh * K;
   const Threshold th = kth_largest(keys, npg, keep, sh);
+  if (tid == 0) KVS_SELECT_STAMP(10);
   place_kept(keys, npg, keep, th, sh, [&](int pos, int p) { out[pos] = p; });
   for (int k = keep + tid; k < K; k += kSelThreads) out[k] = -1;
   if (tid == 0) sel_count[rh] = keep;
+  if (tid == 0) KVS_SELECT_STAMP(11);
 }
 
 template <int D, int GQ, typename DT>
@@ -88,6 +113,16 @@ hipError_t launch_g(const CacheView& c, const void* q, float* scores, int K, int
 }
 
 }  // namespace
+
+#ifdef KVS_WG_STAMPS
+hipError_t copy_select_stamps(uint64_t* dst, size_t blocks, hipStream_t s) {
+  void* src = nullptr;
+  if (hipError_t e = hipGetSymbolAddress(&src, HIP_SYMBOL(g_select_stamps))) return e;
+  if (blocks > (size_t)kSelectStampBlocks) blocks = kSelectStampBlocks;
+  return hipMemcpyAsync(dst, src, blocks * kSelectStamps * sizeof(uint64_t),
+                        hipMemcpyDeviceToDevice, s);
+}
+#endif
 
 hipError_t launch_select(const CacheView& c, const void* q, float* scores, int K, int32_t* sel,
                          int32_t* sel_count, hipStream_t s) {

@@ -146,6 +146,8 @@ def lib() -> ctypes.CDLL:
             L.kvs_decode_stamps_offset.restype = ctypes.c_size_t
             L.kvs_score_stamps.argtypes = [vp, ctypes.c_size_t, vp]
             L.kvs_score_stamps.restype = ctypes.c_int
+            L.kvs_select_stamps.argtypes = [vp, ctypes.c_size_t, vp]
+            L.kvs_select_stamps.restype = ctypes.c_int
         for name in EXPORTS:
             if name not in ("kvs_decode_workspace_bytes", "kvs_prefill_workspace_bytes",
                             "kvs_last_error"):
@@ -601,3 +603,10 @@ def kvs_score_stamps(dst: torch.Tensor, stream=None) -> None:
     """Instrumented build only: clock stamps [waves][3] (entry, share known,
     exit) of the last scoring launch into dst (int64 [waves][3])."""
     _check(lib().kvs_score_stamps(_ptr(dst), dst.shape[0], _stream(stream)))
+
+
+def kvs_select_stamps(dst: torch.Tensor, stream=None) -> None:
+    """Instrumented build only: clock stamps [blocks][12] (entry, up to
+    eight waves' scoring done, past the barrier, K-th key known, exit) of the
+    last one-launch selection."""
+    _check(lib().kvs_select_stamps(_ptr(dst), dst.shape[0], _stream(stream)))

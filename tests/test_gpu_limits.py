@@ -59,6 +59,39 @@ def test_topk_at_page_limit(K):
             assert np.all(sel_h[r, h, len(want):] == -1)
 
 
+@pytest.mark.parametrize("K", [1, 7, 64, MAX_K])
+def test_topk_short_rows_with_ties(K):
+    """Rows from empty to 1500 pages (around the 64- and 1024-item sizes),
+    with scores from a three-value set (ties everywhere), an all-equal row, a
+    row of -inf only and 5% -inf entries.  Exact against the oracle's rule."""
+    require_gpu()
+    say(f"[case] topk short rows K={K}")
+    g = np.random.default_rng(12 + K)
+    lens = [0, 1, 2, 63, 64, 65, 127, 640, 1000, 1023, 1024, 1025, 1500, 17, 5, 300]
+    b, Hkv, maxpg = 2, 8, 1536
+    s = g.choice(np.array([-1.5, 0.25, 3.0], dtype=np.float32), size=(b, Hkv, maxpg))
+    s[g.random(s.shape) < 0.05] = -np.inf
+    s[0, 3, :] = 0.5                       # all equal
+    s[1, 6, :] = -np.inf                   # nothing but -inf
+    n = np.array(lens, dtype=np.int32).reshape(b, Hkv) * P
+    n[1, 0] -= 3                           # a partial last page
+    dev = "cuda"
+    scores = torch.from_numpy(s).to(dev)
+    seq = torch.from_numpy(n).to(dev)
+    sel = torch.full((b, Hkv, K), -7, dtype=torch.int32, device=dev)
+    cnt = torch.full((b, Hkv), -7, dtype=torch.int32, device=dev)
+    kvs.kvs_topk_pages(scores, seq, P, K, sel, cnt)
+    torch.cuda.synchronize()
+    sel_h, cnt_h = sel.cpu().numpy(), cnt.cpu().numpy()
+    for r in range(b):
+        for h in range(Hkv):
+            npg = -(-int(n[r, h]) // P)
+            want = O.topk_pages(s[r, h, :npg], K)
+            assert cnt_h[r, h] == len(want) == min(K, npg)
+            assert np.array_equal(sel_h[r, h, :len(want)], want), f"r={r} h={h} npg={npg}"
+            assert np.all(sel_h[r, h, len(want):] == -1)
+
+
 @pytest.mark.parametrize("topk", [None, MAX_K])
 def test_longest_heads_end_to_end(topk):
     """One request whose heads hold 1 to 131072 tokens (8192 pages): min-max
