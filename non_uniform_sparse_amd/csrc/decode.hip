@@ -1,8 +1,8 @@
-// Ragged split-K flash-decode over head-group page tables, and the
-// log-sum-exp combine of the splits (FlexiCache summary, Core method: sparse
-// flash-decoding over each head's selected pages; Tangram review, 3.2 Ragged
-// Paging and 3.3 AOT Load Balancing: per-group tables and a static split map
-// S with S_i workgroups for group i).
+// Ragged split-K flash-decode over head-group page tables (FlexiCache
+// summary, Core method: sparse flash-decoding over each head's selected
+// pages; Tangram review, 3.2 Ragged Paging and 3.3 AOT Load Balancing:
+// per-group tables and a static split map S with S_i workgroups for group
+// i).  The log-sum-exp combine of the splits is combine.hip.
 //
 // Work decomposition.  For request r and group i the units are (slot, page)
 // pairs, head-major: all attended pages of slot 0, then slot 1, ...  With U
@@ -10,9 +10,9 @@
 // One 64-lane workgroup (one wave) per (r, i, s) walks its units in order,
 // keeping an online softmax per query head of the KV head it is in, and
 // emits a partial (o, lse) for every head it touched, noting for each head
-// whether it is that head's first or last split.  The combine kernel merges,
-// for each query head, the contiguous range of splits that touched its KV
-// head.
+// whether it is that head's first or last split.  The combine kernel
+// (combine.hip) merges, for each query head, the contiguous range of splits
+// that touched its KV head.
 //
 // Lane layout for one page of one head (P = 16 rows of d 16-bit elements):
 // lane l takes channels 8*(l % COLS) .. +8 of rows rg + RPL*k, rg = l / COLS,
@@ -187,146 +187,6 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeArgs a) {
   if (cur_j >= 0) end_head(cur_j);
 }
 
-// Waves per combine workgroup at most: 16 at d = 128; 8 at d = 256, whose
-// rows need twice the registers.
-template <int D>
-constexpr int kCombineWaves = D == 128 ? 16 : 8;
-
-// One workgroup of W = blockDim.x / 64 waves (1 to 16) per (request, query
-// head).  The splits that touched the head form the contiguous range
-// [first, last] that the decode kernel recorded (an empty split inside it
-// carries lse = -inf).  Wave w merges its W-th of the range, 8 splits per
-// step: lane l takes split l / 8 of the step and channels (l % 8) * D/8 ..
-// +D/8, and the wave keeps a running maximum m of the lse it has seen, its
-// weighted sum and its total weight relative to m (a step that raises m
-// rescales both first).  The loads of the next step are in flight while a
-// step is merged, and no pass over the range precedes the merge.  The 8
-// split lanes of each channel chunk are summed with DPP / lane swaps; the
-// waves' (m, sum, weight) meet in LDS and are merged in wave order, so the
-// result does not depend on timing.  A head spanning hundreds of splits
-// (long, full-budget heads) is thus spread over up to 16 waves.
-template <int D>
-__global__ __launch_bounds__(64 * kCombineWaves<D>) void combine_kernel(DecodeArgs a) {
-  constexpr int CH = D / 8;          // channels per lane
-  constexpr int V4 = CH / 4;         // float4 loads per split row
-  constexpr int kMaxWaves = kCombineWaves<D>;
-  __shared__ float s_acc[kMaxWaves][D];
-  __shared__ float s_m[kMaxWaves], s_den[kMaxWaves];
-  const CacheView& c = a.c;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int W = blockDim.x >> 6;
-  const int r = blockIdx.x / c.Hq;
-  const int g = blockIdx.x % c.Hq;
-  const int h = g / c.Gq;
-  const int64_t rh = (int64_t)r * c.Hkv + h;
-  float* dst = a.out + ((int64_t)r * c.Hq + g) * D;
-  // the head's unit count, exactly as the decode kernel forms it
-  const int n = clampi(c.seq_len[rh], 0, P * c.maxpg);
-  int cnt = (n + P - 1) / P;
-  if (a.sel) cnt = min(cnt, clampi(a.sel_count[rh], 0, a.K));
-  const int lo = a.split_lo[rh], hi = a.split_hi[rh];
-  const int s_lo = cnt > 0 ? clampi(lo, 0, a.Smax - 1) : 0;
-  const int s_hi = cnt > 0 ? clampi(hi, s_lo, a.Smax - 1) : -1;
-  const int64_t row = ((int64_t)r * c.Hq + g) * a.Smax;
-  // this wave's part of the range
-  const int per = (s_hi - s_lo + 1 + W - 1) / W;
-  const int w_lo = s_lo + wave * per, w_hi = min(s_hi, w_lo + per - 1);
-  const int sl = lane / 8, dc = lane % 8;
-
-  float acc[CH];
-#pragma unroll
-  for (int e = 0; e < CH; ++e) acc[e] = 0.f;
-  float m = -__builtin_inff(), den = 0.f;
-  // One step: the lse of split s0 + sl and its row slice (an in-bounds row
-  // even past w_hi; such a lane's lse is -inf and its row is never used).
-  auto load = [&](int s0, float& lse, float4 (&x)[V4]) {
-    const int sp = s0 + sl;
-    lse = sp <= w_hi ? a.lse_part[row + sp] : -__builtin_inff();
-    const float4* src =
-        reinterpret_cast<const float4*>(a.o_part + (row + min(sp, w_hi)) * D + dc * CH);
-#pragma unroll
-    for (int v = 0; v < V4; ++v) x[v] = src[v];
-  };
-  auto merge = [&](float lse, const float4 (&x)[V4]) {
-    const float m_new = fmaxf(m, group_max<64>(lse));   // uniform over the wave
-    if (!(m_new > -__builtin_inff())) return;           // nothing valid yet
-    const float keep = m > -__builtin_inff() ? __builtin_amdgcn_exp2f(m - m_new) : 0.f;
-    // an empty split (lse = -inf) weighs 0; its row may hold stale data, so
-    // its contribution is selected away, never multiplied in
-    const float wt = lse > -__builtin_inff() ? __builtin_amdgcn_exp2f(lse - m_new) : 0.f;
-    const bool use = wt > 0.f;
-    den = den * keep + wt;
-#pragma unroll
-    for (int v = 0; v < V4; ++v) {
-      acc[4 * v] = acc[4 * v] * keep + (use ? wt * x[v].x : 0.f);
-      acc[4 * v + 1] = acc[4 * v + 1] * keep + (use ? wt * x[v].y : 0.f);
-      acc[4 * v + 2] = acc[4 * v + 2] * keep + (use ? wt * x[v].z : 0.f);
-      acc[4 * v + 3] = acc[4 * v + 3] * keep + (use ? wt * x[v].w : 0.f);
-    }
-    m = m_new;
-  };
-  if (w_lo <= w_hi) {
-    float l0, l1;
-    float4 x0[V4], x1[V4];
-    load(w_lo, l0, x0);
-    for (int s0 = w_lo; s0 <= w_hi; s0 += 16) {   // no load past w_hi's step (uniform tests)
-      if (s0 + 8 <= w_hi) load(s0 + 8, l1, x1);
-      merge(l0, x0);
-      if (s0 + 16 <= w_hi) load(s0 + 16, l0, x0);
-      if (s0 + 8 <= w_hi) merge(l1, x1);
-    }
-  }
-  // sums over the 8 split lanes of each channel chunk (lanes dc + 8 sl)
-  den += dpp<0x128>(den);   // row_ror:8 -> lane ^ 8 within a row of 16
-  den = across_sum<16>(den);
-#pragma unroll
-  for (int e = 0; e < CH; ++e) {
-    float v = acc[e];
-    v += dpp<0x128>(v);
-    v = across_sum<16>(v);
-    acc[e] = v;
-  }
-  if (W == 1) {   // one wave: its sums are the head's (uniform over the block)
-    if (sl == 0) {
-      const float inv = den > 0.f ? 1.f / den : 0.f;
-      float4* o4 = reinterpret_cast<float4*>(dst + dc * CH);
-#pragma unroll
-      for (int v = 0; v < V4; ++v)
-        o4[v] = make_float4(acc[4 * v] * inv, acc[4 * v + 1] * inv, acc[4 * v + 2] * inv,
-                            acc[4 * v + 3] * inv);
-    }
-    return;
-  }
-  if (sl == 0) {
-#pragma unroll
-    for (int e = 0; e < CH; ++e) s_acc[wave][dc * CH + e] = acc[e];
-  }
-  if (lane == 0) {
-    s_m[wave] = m;
-    s_den[wave] = den;
-  }
-  __syncthreads();
-  // wave 0 merges the waves' sums in wave order, D / 64 channels per lane
-  if (wave == 0) {
-    float M = -__builtin_inff();
-    for (int w = 0; w < W; ++w) M = fmaxf(M, s_m[w]);
-    float dsum = 0.f, x[D / 64];
-#pragma unroll
-    for (int k = 0; k < D / 64; ++k) x[k] = 0.f;
-    if (M > -__builtin_inff()) {
-      for (int w = 0; w < W; ++w) {
-        const float sc = s_m[w] > -__builtin_inff() ? __builtin_amdgcn_exp2f(s_m[w] - M) : 0.f;
-        dsum += sc * s_den[w];
-#pragma unroll
-        for (int k = 0; k < D / 64; ++k) x[k] += sc * s_acc[w][lane + 64 * k];
-      }
-    }
-    const float inv = dsum > 0.f ? 1.f / dsum : 0.f;
-#pragma unroll
-    for (int k = 0; k < D / 64; ++k) dst[lane + 64 * k] = x[k] * inv;
-  }
-}
-
 template <int D, int GQ, typename DT>
 hipError_t launch_decode_v(const DecodeArgs& a, hipStream_t s) {
   const int64_t blocks = (int64_t)a.c.b * a.splits_total;
@@ -365,19 +225,6 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   if (a.c.dtype == KVS_F16)
     return a.c.d == 128 ? launch_decode_g<128, F16>(a, s) : launch_decode_g<256, F16>(a, s);
   return a.c.d == 128 ? launch_decode_g<128, BF16>(a, s) : launch_decode_g<256, BF16>(a, s);
-}
-
-hipError_t launch_combine(const DecodeArgs& a, hipStream_t s) {
-  const int64_t blocks = (int64_t)a.c.b * a.c.Hq;
-  // one wave per 24 splits a head can span (a group's splits), at most
-  // kCombineWaves
-  const int per = (a.Smax + 23) / 24;
-  const int waves = std::max(1, std::min(a.c.d == 128 ? kCombineWaves<128> : kCombineWaves<256>, per));
-  if (a.c.d == 128)
-    hipLaunchKernelGGL((combine_kernel<128>), dim3((unsigned)blocks), dim3(64 * waves), 0, s, a);
-  else
-    hipLaunchKernelGGL((combine_kernel<256>), dim3((unsigned)blocks), dim3(64 * waves), 0, s, a);
-  return hipGetLastError();
 }
 
 hipError_t decode_blocks_per_cu(int d, int gqa, int dtype, int* blocks) {
