@@ -234,9 +234,9 @@ int kvs_append_kv(const kvs_paged_kv* cache, const void* k_new, const void* v_ne
  * in its group's pages [T 3.2], update the min-max bounds of every page they
  * land in [F Key observations, assumption 2] (merged with the bounds the
  * first page already held), and set seq_len[r][h] = n + q.  q is clamped to
- * [0, min(C, P*max_group_pages - n)].  The quota is the caller's: under the
- * reading used here, chunk [a, e) of an N-token prompt keeps
- * ceil(B e) - ceil(B a) tokens, ceil(B N) in all.
+ * [0, min(C, P*max_group_pages - n)].  The quota is an input; the reading
+ * used here, chunk [a, e) of an N-token prompt keeps ceil(B e) - ceil(B a)
+ * tokens (ceil(B N) in all), is what kvs_prefill_quota computes.
  *   k_chunk, v_chunk  device, [b][Hkv][C][d] dtype, 16-byte aligned.
  *   scores            device, [b][Hkv][C] fp32 (integer keys from the fp32
  *                     bits, as in kvs_topk_pages).
@@ -260,6 +260,41 @@ int kvs_prefill_chunk(const kvs_paged_kv* cache, const void* k_chunk, const void
 /* Bytes of workspace kvs_prefill_chunk needs (per head: its length before
  * the chunk, its quota and the kept positions).  0 on bad arguments. */
 size_t kvs_prefill_workspace_bytes(int32_t b, int32_t Hkv, int32_t C);
+
+/*
+ * Budget Reservation quota of one prefill chunk, host only [T 3.1: every
+ * head keeps Top(ceil(B N), s) of its N-token prompt, chunk by chunk, so its
+ * footprint is fixed when the request is scheduled].  Reading: after the
+ * first x tokens a head has kept ceil(B x) (0 for x = 0), so the chunk of
+ * positions [start, start + chunk) keeps, for request r and head h,
+ *   quota[r][h] = ceil(B_h e) - ceil(B_h a),
+ *   a = min(N_r, start), e = min(N_r, start + chunk),
+ * which telescopes to ceil(B_h N_r) over all chunks and never exceeds the
+ * chunk's length.  The ceiling is taken on the exact binary value of B_h
+ * (integer arithmetic, no rounding).
+ *   budgets   host, [Hkv] double in (0, 1]: one layer's head budgets.
+ *   contexts  host, [b] int64 in [1, 2^40]: prompt length per request.
+ *   start     first position of the chunk, 0 <= start <= 2^40; chunk >= 1.
+ *   quota     host out, [b][Hkv] int32 (the input of kvs_prefill_chunk,
+ *             once copied to the device).
+ * KVS_EINVAL on a null pointer or any value out of range, before any write.
+ */
+int kvs_prefill_quota(const double* budgets, const int64_t* contexts, int32_t b, int32_t Hkv,
+                      int64_t start, int32_t chunk, int32_t* quota);
+
+/*
+ * Heads that re-select their pages at a decode step, host only [F Method:
+ * heads whose attention is stable over steps reuse their page selection
+ * between periodic reranks; the others re-select every step].  Reading:
+ * steps count from the first decode step (step 0), which always selects, so
+ *   due[h] = (step % period == 0) || !stable[h].
+ *   stable   host, [Hkv] bytes, nonzero = stable head.
+ *   due      host out, [Hkv] bytes, 1 = re-select (the head mask of
+ *            kvs_score_pages_heads / kvs_topk_pages_heads).
+ * KVS_EINVAL on a null pointer, Hkv < 1, step < 0 or period < 1.
+ */
+int kvs_rerank_heads(const uint8_t* stable, int32_t Hkv, int32_t step, int32_t period,
+                     uint8_t* due);
 
 /*
  * Host tier of a cache whose stable heads keep only their selected pages on

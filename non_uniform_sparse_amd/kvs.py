@@ -32,7 +32,7 @@ EXPORTS = (
     "kvs_codec_bounds", "kvs_codec_encode", "kvs_codec_decode",
     "kvs_gather_probe", "kvs_gather_probe_sink_words", "kvs_stream_probe",
     "kvs_stream_probe_sink_words",
-    "kvs_plan_split",
+    "kvs_plan_split", "kvs_prefill_quota", "kvs_rerank_heads",
     "kvs_decode_attn", "kvs_decode_splits", "kvs_decode_combine", "kvs_decode_attn_noalloc",
     "kvs_decode_workspace_bytes", "kvs_decode_concurrency", "kvs_cluster_heads",
     "kvs_last_error",
@@ -133,6 +133,8 @@ def lib() -> ctypes.CDLL:
         L.kvs_stream_probe.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_size_t, vp]
         L.kvs_stream_probe_sink_words.argtypes = [ctypes.POINTER(i32)]
         L.kvs_plan_split.argtypes = [vp, vp, i32, i32, i32, f64, i32, vp]
+        L.kvs_prefill_quota.argtypes = [vp, vp, i32, i32, ctypes.c_int64, i32, vp]
+        L.kvs_rerank_heads.argtypes = [vp, i32, i32, i32, vp]
         for name in ("kvs_decode_attn", "kvs_decode_splits", "kvs_decode_combine"):
             getattr(L, name).argtypes = [pkv, vp, vp, vp, i32, vp, f32, vp, ctypes.c_size_t, vp, vp]
         L.kvs_decode_attn_noalloc.argtypes = [pkv, vp, vp, vp, i32, vp, f32, vp, vp]
@@ -490,6 +492,31 @@ def kvs_prefill_chunk(cache: Cache, k_chunk: torch.Tensor, v_chunk: torch.Tensor
     nbytes = workspace.numel() * workspace.element_size()
     _check(lib().kvs_prefill_chunk(ctypes.byref(s), _ptr(k_chunk), _ptr(v_chunk), _ptr(scores),
                                    _ptr(quota), int(C), _ptr(workspace), nbytes, _stream(stream)))
+
+
+def kvs_prefill_quota(budgets: np.ndarray, contexts: np.ndarray, start: int,
+                      chunk: int) -> np.ndarray:
+    """[b][Hkv] int32 tokens each head keeps from prompt positions
+    [start, start + chunk), for one layer's budgets [Hkv]."""
+    B = np.ascontiguousarray(budgets, dtype=np.float64)
+    N = np.ascontiguousarray(contexts, dtype=np.int64)
+    if B.ndim != 1 or N.ndim != 1:
+        raise ValueError("budgets [Hkv] and contexts [b] must be one-dimensional")
+    q = np.zeros((N.shape[0], B.shape[0]), dtype=np.int32)
+    _check(lib().kvs_prefill_quota(B.ctypes.data, N.ctypes.data, N.shape[0], B.shape[0],
+                                   int(start), int(chunk), q.ctypes.data))
+    return q
+
+
+def kvs_rerank_heads(stable: np.ndarray, step: int, period: int) -> np.ndarray:
+    """[Hkv] bool: the heads that re-select their pages at decode step ``step``."""
+    st = np.ascontiguousarray(np.asarray(stable, dtype=bool).astype(np.uint8))
+    if st.ndim != 1:
+        raise ValueError("stable must be one-dimensional")
+    due = np.zeros(st.shape[0], dtype=np.uint8)
+    _check(lib().kvs_rerank_heads(st.ctypes.data, st.shape[0], int(step), int(period),
+                                  due.ctypes.data))
+    return due.astype(bool)
 
 
 def kvs_plan_split(budgets: np.ndarray, head_slot: np.ndarray, Hp: int, cap: float,

@@ -17,7 +17,6 @@ head's ragged pages and the pages' min-max bounds happen in one kernel.
 from __future__ import annotations
 
 import math
-from fractions import Fraction
 from typing import List, Tuple
 
 import numpy as np
@@ -27,15 +26,7 @@ from . import kvs
 from .pipeline import DecodeStep
 from .workloads import Workload, _mix, torch_dtype
 
-__all__ = ["ChunkedPrefill", "kept_after"]
-
-
-def kept_after(budget: float, x: int) -> int:
-    """Tokens a head has kept once x prompt tokens are in: ceil(B x), on the
-    exact binary value of B."""
-    if x <= 0:
-        return 0
-    return math.ceil(Fraction(budget) * x)
+__all__ = ["ChunkedPrefill"]
 
 
 class ChunkedPrefill:
@@ -49,11 +40,11 @@ class ChunkedPrefill:
         if not 1 <= chunk <= 8192:
             raise ValueError("chunk length must lie in [1, 8192]")
         self.wl, self.cfg, self.device, self.C = wl, c, device, chunk
-        for r in range(c.b):
-            for l in range(c.L):
-                for h in range(c.Hkv):
-                    if kept_after(float(wl.budgets[l, h]), int(wl.contexts[r])) != wl.n[r, l, h]:
-                        raise ValueError("the reserved length differs from ceil(B N)")
+        whole = int(wl.contexts.max())
+        for l in range(c.L):   # the quota of a chunk covering every prompt: ceil(B N)
+            if not np.array_equal(kvs.kvs_prefill_quota(wl.budgets[l], wl.contexts, 0, whole),
+                                  wl.n[:, l, :]):
+                raise ValueError("the reserved length differs from ceil(B N)")
         # the reservation: every head's pages and bounds blocks for n = ceil(B N)
         self.ds = DecodeStep(wl, device=device, poison=True)
         self.chunks = int(-(-int(wl.contexts.max()) // chunk))
@@ -67,15 +58,7 @@ class ChunkedPrefill:
 
     def quota(self, l: int, k: int) -> np.ndarray:
         """[b][Hkv] tokens each head keeps from chunk k of layer l."""
-        c, wl = self.cfg, self.wl
-        q = np.zeros((c.b, c.Hkv), dtype=np.int32)
-        for r in range(c.b):
-            N = int(wl.contexts[r])
-            a, e = min(N, k * self.C), min(N, (k + 1) * self.C)
-            for h in range(c.Hkv):
-                B = float(wl.budgets[l, h])
-                q[r, h] = kept_after(B, e) - kept_after(B, a)
-        return q
+        return kvs.kvs_prefill_quota(self.wl.budgets[l], self.wl.contexts, k * self.C, self.C)
 
     def inputs(self, l: int, k: int) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
         """Chunk k of layer l: keys and values [b][Hkv][C][d] ~ N(0,1) and

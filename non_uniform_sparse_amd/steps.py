@@ -34,11 +34,8 @@ __all__ = ["DecodeLoop", "heads_due"]
 def heads_due(t: int, stable: np.ndarray, period: int) -> np.ndarray:
     """KV heads that re-select their pages at step t (counted from the first
     decode step): every head on a rerank step (t a multiple of the period),
-    otherwise the unstable ones."""
-    stable = np.asarray(stable, dtype=bool)
-    if t % period == 0:
-        return np.ones(stable.shape, dtype=bool)
-    return ~stable
+    otherwise the unstable ones (kvs_rerank_heads)."""
+    return kvs.kvs_rerank_heads(stable, t, period)
 
 
 class DecodeLoop:

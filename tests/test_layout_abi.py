@@ -308,12 +308,68 @@ def test_fused_selection_policy():
 
 
 def test_rerank_schedule_matches_oracle():
+    """kvs_rerank_heads (and the loop's heads_due, which calls it) against
+    the oracle's rerank_due, and its argument checks."""
     from non_uniform_sparse_amd.steps import heads_due
     stable = np.array([True, False, True, True, False, True, True, True])
     for period in (1, 4, 16):
         for t in range(40):
             want = [O.rerank_due(t, bool(s), period) for s in stable]
+            assert kvs.kvs_rerank_heads(stable, t, period).tolist() == want
             assert heads_due(t, stable, period).tolist() == want
+    L = _lib()
+    st = np.ones(8, dtype=np.uint8)
+    due = np.zeros(8, dtype=np.uint8)
+    for args in [(st.ctypes.data, 8, -1, 16), (st.ctypes.data, 8, 0, 0), (st.ctypes.data, 0, 0, 16),
+                 (None, 8, 0, 16)]:
+        assert L.kvs_rerank_heads(*args, due.ctypes.data) == kvs.KVS_EINVAL
+    assert L.kvs_rerank_heads(st.ctypes.data, 8, 0, 16, None) == kvs.KVS_EINVAL
+
+
+def test_prefill_quota_matches_oracle():
+    """kvs_prefill_quota bit for bit against the oracle's chunk_quota (exact
+    rationals) on budgets that are short binary fractions, decimal fractions
+    with long expansions, values just below and above such points, the
+    smallest normal doubles and 1; prompts ending inside, at and before a
+    chunk; and the quotas telescoping to ceil(B N)."""
+    g = np.random.default_rng(21)
+    special = [1.0, 0.5, 0.25, 0.1, 1 / 3, 2 / 3, 0.999999, np.nextafter(0.5, 0), np.nextafter(0.5, 1),
+               np.nextafter(1.0, 0), 2.0 ** -30, 2.0 ** -1000, 5e-324 * 2 ** 60, 0.3, 0.7]
+    for trial in range(60):
+        Hkv = int(g.integers(1, 9))
+        B = np.array([special[int(g.integers(len(special)))] if g.random() < 0.5 else
+                      float(g.uniform(1e-6, 1.0)) for _ in range(Hkv)])
+        b = int(g.integers(1, 5))
+        N = g.integers(1, 40000, size=b).astype(np.int64)
+        if trial % 7 == 0:
+            N[0] = 2 ** 40                     # the largest context
+        chunk = int(g.choice([1, 7, 2048, 4096, 65536]))
+        for start in [0, chunk, 3 * chunk, int(N.max()) - 1, int(N.max()) + 5]:
+            start = min(max(0, start), 2 ** 40)
+            q = kvs.kvs_prefill_quota(B, N, start, chunk)
+            for r in range(b):
+                a, e = min(int(N[r]), start), min(int(N[r]), start + chunk)
+                for h in range(Hkv):
+                    assert q[r, h] == O.chunk_quota(float(B[h]), a, e), (B[h], a, e)
+    # telescoping over a whole prompt
+    B = np.array([0.1, 1 / 3, 0.999999, 1.0])
+    N = np.array([1, 2047, 2048, 2049, 100003], dtype=np.int64)
+    tot = sum(kvs.kvs_prefill_quota(B, N, k * 2048, 2048) for k in range(-(-int(N.max()) // 2048)))
+    for r in range(len(N)):
+        for h in range(len(B)):
+            assert tot[r, h] == O.retained_count(float(B[h]), int(N[r]))
+    L = _lib()
+    q = np.zeros((2, 2), dtype=np.int32)
+    good = (np.array([0.5, 0.5]), np.array([10, 10], dtype=np.int64))
+    call = lambda B_, N_, start=0, chunk=4: L.kvs_prefill_quota(B_.ctypes.data, N_.ctypes.data, len(N_),
+                                                                len(B_), start, chunk, q.ctypes.data)
+    assert call(*good) == kvs.KVS_OK
+    assert call(np.array([0.0, 0.5]), good[1]) == kvs.KVS_EINVAL
+    assert call(np.array([1.5, 0.5]), good[1]) == kvs.KVS_EINVAL
+    assert call(np.array([np.nan, 0.5]), good[1]) == kvs.KVS_EINVAL
+    assert call(good[0], np.array([0, 10], dtype=np.int64)) == kvs.KVS_EINVAL
+    assert call(*good, start=-1) == kvs.KVS_EINVAL
+    assert call(*good, chunk=0) == kvs.KVS_EINVAL
 
 
 # ------------------------------------------------------------ host tier --
