@@ -135,3 +135,28 @@ def test_heads_without_tokens(topk):
     if topk:
         cnt = step.bufs[0].sel_count.cpu().numpy()
         assert np.array_equal(cnt == 0, wl.n[:, 0, :] == 0)
+
+
+def test_long_runs_of_empty_heads():
+    """Scoring deals all heads' pages out evenly, and a wave that finishes a
+    head looks for the next one that holds pages, 64 heads per probe: here
+    runs of 8, 63, 64, 65 and 130 heads without tokens (whole requests of 8
+    heads, and a run cut inside a request) lie between heads that hold 1 to
+    60 pages, so shares start, end and resume on both sides of every run.
+    Scores, selections and outputs against the oracle."""
+    require_gpu()
+    b, Hkv = 48, 8
+    wl = make_workload("llama8b_ragged", b=b, N=960, Hq=32, d=128, dtype="bf16", Hp=2, topk=5)
+    g = np.random.default_rng(31)
+    n = g.integers(1, 961, size=(b, Hkv))
+    flat = n.reshape(-1)
+    for lo, run in [(3, 8), (20, 63), (100, 64), (180, 65), (250, 130)]:
+        flat[lo:lo + run] = 0
+    flat[90] = 1          # a single-token head between two runs
+    wl.n[:, 0, :] = flat.reshape(b, Hkv)
+    say(f"[case] long runs of empty heads: {int((flat == 0).sum())} empty of {flat.size}")
+    step = DecodeStep(wl, device="cuda")
+    st = Stats()
+    check_layer(step, 0, step.queries()[0], range(b), st)
+    assert_output_bar(st, "long runs of empty heads")
+
