@@ -160,3 +160,23 @@ def test_long_runs_of_empty_heads():
     check_layer(step, 0, step.queries()[0], range(b), st)
     assert_output_bar(st, "long runs of empty heads")
 
+
+@pytest.mark.parametrize("b", [300, 2047])
+def test_scoring_at_many_heads(b):
+    """b * Hkv = 2 400 and 16 376 heads (the documented limit is 16 383):
+    the scoring kernel's page-count scan then loops over several batches of
+    heads, and at the limit its LDS holds 64 KB of prefix.  Short heads
+    (0 to 64 tokens), top-2; scores, selections and outputs of a seeded
+    sample of requests against the oracle."""
+    require_gpu()
+    Hkv = 8
+    wl = make_workload("llama8b_ragged", b=b, N=64, Hq=32, d=128, dtype="bf16", Hp=2, topk=2)
+    g = np.random.default_rng(41)
+    wl.n[:, 0, :] = g.integers(0, 65, size=(b, Hkv))
+    say(f"[case] scoring at {b * Hkv} heads")
+    step = DecodeStep(wl, device="cuda")
+    st = Stats()
+    sample = sorted(set([0, 1, b // 2, b - 2, b - 1] + g.integers(0, b, size=12).tolist()))
+    check_layer(step, 0, step.queries()[0], sample, st)
+    assert_output_bar(st, f"scoring at {b * Hkv} heads")
+
