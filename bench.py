@@ -2,8 +2,12 @@
 
 A step is one full decode step of the workload: for every layer, page
 scores -> top-K pages (top-K workloads only) -> ragged split-K decode + LSE
-combine, all on one stream.  Inputs (caches, min-max metadata, queries) are
-resident in HBM before the timed region starts.  Prints one JSON line.
+combine, captured once as a HIP graph and replayed (the requests may be cut
+into micro-batches whose layer chains run on streams of their own).  Inputs
+(caches, min-max metadata, queries) are resident in HBM before the timed
+region starts.  The roofline object is the dominant kernel's, the split-K
+decode timed alone in whole-batch launches; every other kernel of the path
+has a row of its own.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
 """
