@@ -98,25 +98,28 @@ __device__ __forceinline__ FlatShare flat_share(const int* pre, int BH) {
 }
 
 // Resident blocks of kFlatThreads threads for `kernel` on the current
-// device (compute units x blocks per unit), found once per device.
+// device (compute units x blocks per unit, at most max_per_cu per unit),
+// the occupancy found once per device.
 template <const void* (*Sym)()>
-hipError_t resident_grid(int* grid) {
+hipError_t resident_grid(int* grid, int max_per_cu = 1 << 20) {
   constexpr int kMaxDevices = 64;
-  static std::atomic<int> grid_of[kMaxDevices];
+  static std::atomic<int> cus_of[kMaxDevices], per_cu_of[kMaxDevices];
   int dev = 0;
   if (hipError_t e = hipGetDevice(&dev)) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
-  int g = grid_of[dev].load(std::memory_order_relaxed);
-  if (g == 0) {
-    int cus = 0, per_cu = 0;
+  int cus = cus_of[dev].load(std::memory_order_relaxed);
+  int per_cu = per_cu_of[dev].load(std::memory_order_relaxed);
+  if (cus == 0 || per_cu == 0) {
     if (hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev))
       return e;
     if (hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, Sym(), kFlatThreads, 0))
       return e;
-    g = max(1, cus * max(1, per_cu));
-    grid_of[dev].store(g, std::memory_order_relaxed);
+    cus = max(1, cus);
+    per_cu = max(1, per_cu);
+    per_cu_of[dev].store(per_cu, std::memory_order_relaxed);
+    cus_of[dev].store(cus, std::memory_order_relaxed);
   }
-  *grid = g;
+  *grid = cus * max(1, min(per_cu, max_per_cu));
   return hipSuccess;
 }
 

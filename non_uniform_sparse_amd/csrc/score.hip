@@ -8,7 +8,8 @@
 // The work is a stream: every head's bounds are one contiguous run of
 // 4*d-byte blocks (block meta_base[r][h] + p), and the read is bound by HBM.
 // Heads differ widely in page count, so the grid is sized to what the chip
-// holds at once and the pages are dealt out evenly: each block first forms
+// holds at once (at most two blocks per compute unit) and the pages are
+// dealt out evenly: each block first forms
 // the prefix sum of the heads' page counts in LDS (and copies the head-slot
 // table there); wave w of W then takes flat pages [T*w/W, T*(w+1)/W) of the
 // T in all heads, one segment per head it touches.
@@ -218,11 +219,18 @@ const void* score_symbol() {
   return reinterpret_cast<const void*>(&score_kernel<D, GQ, DT>);
 }
 
+// Blocks per compute unit at most.  A full resident grid (three blocks per
+// unit at d = 256) scores a whole batch no faster than two, and in a step
+// whose request micro-batches run on streams of their own, where score
+// launches share the chip with the other parts' decode waves, two or one
+// per unit made the whole step faster than three.
+constexpr int kScoreBlocksPerCu = 2;
+
 template <int D, int GQ, typename DT>
 hipError_t launch_v(const CacheView& c, const void* q, float* scores, const HeadMask& heads,
                     hipStream_t s) {
-  int grid = 0;   // one resident wave per slot
-  if (hipError_t e = resident_grid<score_symbol<D, GQ, DT>>(&grid)) return e;
+  int grid = 0;   // resident blocks, at most kScoreBlocksPerCu per compute unit
+  if (hipError_t e = resident_grid<score_symbol<D, GQ, DT>>(&grid, kScoreBlocksPerCu)) return e;
   const size_t lds = (size_t)(c.b * c.Hkv + 1) * sizeof(int);
   hipLaunchKernelGGL((score_kernel<D, GQ, DT>), dim3((unsigned)grid), dim3(kThreads), lds, s, c,
                      static_cast<const uint16_t*>(q), scores, heads);
