@@ -45,10 +45,10 @@ def default_microbatches(wl: Workload) -> int:
     """Request micro-batches for the step graph.  Parts only overlap once
     their layer chains drift apart; with a single layer (or a few) every part
     runs the same phase at the same time and the split only adds launches
-    (measured: one-layer steps are fastest unsplit, 32- and 48-layer steps
-    fastest with 2-3 parts)."""
+    (measured: one-layer steps are fastest unsplit; the 32- and 48-layer
+    steps fastest with 2 parts, 1-2% ahead of 3 and further ahead of 4)."""
     c = wl.cfg
-    return 1 if c.L < 4 else min(3, c.b)
+    return 1 if c.L < 4 else min(2, c.b)
 
 
 def topk_cap(wl: Workload) -> float:

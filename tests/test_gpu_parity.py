@@ -13,15 +13,19 @@ import oracle as O
 from gpu_harness import (OUT_MAX_ABS, SCORE_TOL, Stats, assert_output_bar, check_layer,
                          require_gpu, say)
 from non_uniform_sparse_amd import kvs
-from non_uniform_sparse_amd.pipeline import DecodeStep
+from non_uniform_sparse_amd.pipeline import DecodeStep, default_microbatches
 from non_uniform_sparse_amd.workloads import make_workload
 
 pytestmark = pytest.mark.gpu
 
 
 def _full(name, microbatches=1, **ov):
+    """The workload at full size (or with overrides); microbatches=None takes
+    the bench's own default for it."""
     require_gpu()
     wl = make_workload(name, **ov)
+    if microbatches is None:
+        microbatches = default_microbatches(wl)
     say(f"[case] {name} {ov} building caches")
     step = DecodeStep(wl, device="cuda", microbatches=microbatches)
     say(f"[case] {name}: W={step.W} T={step.T} S[0]={step.S[0].tolist()}")
@@ -53,12 +57,13 @@ _SAMPLED = [
 @pytest.mark.parametrize("name,requests,layers", _SAMPLED,
                          ids=[f"{n}-L{r.start}-{r.stop - 1}" for n, _, r in _SAMPLED])
 def test_workload_sampled(name, requests, layers):
-    """Full-size caches and the step as the bench runs it (three request
-    micro-batches on three streams); the sampled requests of every layer of
-    the chunk against the oracle.  The chunk starting at layer 0 also
-    replays the step as a captured graph and checks every layer's output
-    bit for bit against the eager step."""
-    wl, step = _full(name, microbatches=3)
+    """Full-size caches and the step as the bench runs it (its request
+    micro-batches, each on a stream of its own); the sampled requests of
+    every layer of the chunk against the oracle.  The chunk starting at
+    layer 0 also replays the step as a captured graph and checks every
+    layer's output bit for bit against the eager step."""
+    wl, step = _full(name, microbatches=None)
+    assert len(step.parts) > 1
     st = Stats()
     qs = step.queries()
     step.run(qs)                       # every layer runs, as in the bench
