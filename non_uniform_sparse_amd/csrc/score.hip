@@ -8,7 +8,7 @@
 // The work is a stream: every head's bounds are one contiguous run of
 // 4*d-byte blocks (block meta_base[r][h] + p), and the read is bound by HBM.
 // Heads differ widely in page count, so the grid is sized to what the chip
-// holds at once (at most two blocks per compute unit) and the pages are
+// holds at once (one block per compute unit) and the pages are
 // dealt out evenly: each block first forms
 // the prefix sum of the heads' page counts in LDS (and copies the head-slot
 // table there); wave w of W then takes flat pages [T*w/W, T*(w+1)/W) of the
@@ -220,11 +220,12 @@ const void* score_symbol() {
 }
 
 // Blocks per compute unit at most.  A full resident grid (three blocks per
-// unit at d = 256) scores a whole batch no faster than two, and in a step
+// unit at d = 256) scores a whole batch no faster than one, and in a step
 // whose request micro-batches run on streams of their own, where score
-// launches share the chip with the other parts' decode waves, two or one
-// per unit made the whole step faster than three.
-constexpr int kScoreBlocksPerCu = 2;
+// launches share the chip with the other parts' decode waves, one block per
+// unit leaves those waves the most room and makes the whole step fastest.
+// A small launch alone on the chip would stream faster with two.
+constexpr int kScoreBlocksPerCu = 1;
 
 template <int D, int GQ, typename DT>
 hipError_t launch_v(const CacheView& c, const void* q, float* scores, const HeadMask& heads,
